@@ -1,0 +1,387 @@
+"""CPU oracle for the Stem block-sparse causal prefill path.  TEST INFRASTRUCTURE.
+
+This module is the plain, slow, obviously-correct definition that the HIP path
+is checked against.  Only the tests, the smoke check and the CPU-baseline leg
+of the benchmark may import it; the library never calls it and never falls
+back to it.  It shares no code with the GPU path.  Everything is NumPy in
+float64 (inputs are upcast exactly from the bf16 / fp32 values the GPU reads),
+and the loops follow the method's stages in the order the pages give them.
+
+Sources.  All five pages carry the title "Stem: Rethinking Causal Information
+Flow in Sparse Attention" (arXiv 2603.06274); they are told apart here by host
+and language:
+  [es] gist.science, Spanish  - "Resumen tecnico" sections 1, 2.A, 2.B, "Implementacion"
+  [it] gist.science, Italian  - "Sommario tecnico" sections 2.A, 2.B, 2.C
+  [nl] gist.science, Dutch    - "Technische samenvatting": Methodologie, Implementatie
+  [fr] gist.science, French   - "Resume technique" sections 1, 2.A, 2.B, 2.C
+  [shd] shd-paper.top, Chinese - method detail section and the English abstract
+
+The pages describe a three-stage pipeline ([es] "Implementacion", [nl]
+"Implementatie", [fr] 2.C): (1) downsample Q, K and a V magnitude to block
+level, (2) fix a per-query-block budget by the Token Position-Decay rule,
+(3) keep the top blocks under the Output-Aware Metric and run exact softmax
+attention over those blocks only.  Where the pages leave a step open, the
+reading taken is stated in the function that implements it:
+
+  * pooling: arithmetic mean of Q and of K over a block's tokens; the block's
+    V magnitude is the mean of the per-token L2 norms (the pages only say
+    "block-level Q, K and V magnitude"; [nl] mentions a max-pooled V
+    magnitude, kept as a variant);
+  * metric: m_ij = softmax_j(qbar_i . kbar_j / sqrt(d)) * w_j over the causal
+    key blocks j <= i.  Inside one row log m_ij = s_ij + log w_j - log Z_i,
+    so it orders blocks exactly like the pages' additive form
+    s_ij + beta*max(0, log ||V_j||^2) with beta = 1/2 whenever log w_j^2 > 0
+    ([es] 2.B equation, [fr] 2.B equation);
+  * budget: k_dyn(i) = max(k_min, ceil(rho0 * exp(-i/tau) * (i+1))) plus the
+    S sink blocks plus the diagonal block, capped at the i+1 causal blocks
+    (the pages give a decay from a high to a low budget: linear in [es] 2.A,
+    [fr] 2.A, exponential in [shd]);
+  * ties in the metric go to the smaller block index, NaN ranks last;
+  * every token of query block i attends to the union of i's selected key
+    blocks, with the token-level causal mask applied inside the diagonal
+    block only;
+  * a final partial block (sequence length not a multiple of the block size)
+    pools over its valid tokens only.
+"""
+from __future__ import annotations
+
+import math
+from typing import Iterable, List, Optional, Sequence, Tuple
+
+import numpy as np
+
+
+# ----------------------------------------------------------------------------
+# block layout
+
+
+def block_layout(cu_seqlens: Sequence[int], block: int) -> np.ndarray:
+    """cu_blocks[s] = first global block of sequence s (ceil(len/block) each)."""
+    cu = np.asarray(cu_seqlens, dtype=np.int64)
+    nb = [(int(cu[s + 1] - cu[s]) + block - 1) // block for s in range(len(cu) - 1)]
+    return np.concatenate([[0], np.cumsum(nb)]).astype(np.int64) if nb else np.zeros(1, np.int64)
+
+
+def tri(n: int) -> int:
+    return n * (n + 1) // 2
+
+
+def score_offsets(cu_blocks: np.ndarray) -> Tuple[np.ndarray, int]:
+    """Start of each sequence's packed lower triangle inside one head, and
+    the per-head total.  Row i of a sequence starts tri(i) further on."""
+    nbs = np.diff(cu_blocks)
+    offs = np.zeros(len(nbs) + 1, dtype=np.int64)
+    for s, n in enumerate(nbs):
+        offs[s + 1] = offs[s] + tri(int(n))
+    return offs, int(offs[-1])
+
+
+# ----------------------------------------------------------------------------
+# stage 1: downsampling ([es] "Implementacion" step 1, [nl] "Implementatie"
+# step 1, [it] 2.C, [fr] 2.C step 1)
+
+
+def pool_mean(x: np.ndarray, cu_seqlens: Sequence[int], block: int) -> np.ndarray:
+    """Block mean of x [T, H, d] -> [H, nbT, d] (float64).
+
+    Block j of sequence s covers its tokens [j*B, min((j+1)*B, len_s)); the
+    mean is over the tokens actually present."""
+    cu = np.asarray(cu_seqlens, dtype=np.int64)
+    cub = block_layout(cu, block)
+    T, H, d = x.shape
+    out = np.zeros((H, int(cub[-1]), d), dtype=np.float64)
+    for s in range(len(cu) - 1):
+        a, e = int(cu[s]), int(cu[s + 1])
+        for jl in range(int(cub[s + 1] - cub[s])):
+            t0 = a + jl * block
+            t1 = min(t0 + block, e)
+            seg = x[t0:t1].astype(np.float64)          # [n, H, d]
+            out[:, int(cub[s]) + jl, :] = seg.sum(axis=0) / (t1 - t0)
+    return out
+
+
+def pool_vnorm(v: np.ndarray, cu_seqlens: Sequence[int], block: int,
+               mode: str = "mean") -> np.ndarray:
+    """Block V magnitude w [Hkv, nbT]: mean (default) or max over the block's
+    tokens of the token's L2 norm ||v_t||_2."""
+    cu = np.asarray(cu_seqlens, dtype=np.int64)
+    cub = block_layout(cu, block)
+    T, H, d = v.shape
+    out = np.zeros((H, int(cub[-1])), dtype=np.float64)
+    for s in range(len(cu) - 1):
+        a, e = int(cu[s]), int(cu[s + 1])
+        for jl in range(int(cub[s + 1] - cub[s])):
+            t0 = a + jl * block
+            t1 = min(t0 + block, e)
+            seg = v[t0:t1].astype(np.float64)
+            norms = np.sqrt((seg * seg).sum(axis=2))   # [n, H]
+            if mode == "mean":
+                out[:, int(cub[s]) + jl] = norms.sum(axis=0) / (t1 - t0)
+            elif mode == "max":
+                out[:, int(cub[s]) + jl] = norms.max(axis=0)
+            else:
+                raise ValueError(mode)
+    return out
+
+
+# ----------------------------------------------------------------------------
+# Output-Aware Metric ([es] 2.B equation and text, [it] 2.B, [nl] OAM,
+# [fr] 2.B): routing relevance of the block times the magnitude of its values
+
+
+def score(qbar: np.ndarray, kbar: np.ndarray, w: np.ndarray,
+          cu_blocks: np.ndarray, head_dim: int) -> np.ndarray:
+    """Packed lower-triangular metric m [Hq, tri_total] (float64).
+
+    For query head h (KV head g = h // (Hq/Hkv)), sequence s and local query
+    block i, the row holds, for j = 0..i (local key blocks):
+        s_ij = qbar_i . kbar_j / sqrt(head_dim)
+        p_ij = exp(s_ij - max_j s) / sum_j exp(s_ij - max_j s)
+        m_ij = p_ij * w_j
+    """
+    Hq = qbar.shape[0]
+    Hkv = kbar.shape[0]
+    G = Hq // Hkv
+    offs, total = score_offsets(cu_blocks)
+    out = np.zeros((Hq, total), dtype=np.float64)
+    scale = 1.0 / math.sqrt(head_dim)
+    for h in range(Hq):
+        g = h // G
+        for s in range(len(cu_blocks) - 1):
+            b0 = int(cu_blocks[s])
+            nb = int(cu_blocks[s + 1]) - b0
+            for i in range(nb):
+                logits = kbar[g, b0:b0 + i + 1, :] @ qbar[h, b0 + i, :] * scale
+                p = np.exp(logits - logits.max())
+                p /= p.sum()
+                row0 = int(offs[s]) + tri(i)
+                out[h, row0:row0 + i + 1] = p * w[g, b0:b0 + i + 1]
+    return out
+
+
+def score_row(m: np.ndarray, cu_blocks: np.ndarray, h: int, s: int, i: int) -> np.ndarray:
+    offs, _ = score_offsets(cu_blocks)
+    row0 = int(offs[s]) + tri(i)
+    return m[h, row0:row0 + i + 1]
+
+
+# ----------------------------------------------------------------------------
+# Token Position-Decay budget ([es] 2.A, [it] 2.A, [nl] TPD, [fr] 2.A; the
+# exponential decay of [shd] method detail); one budget per query block
+# ([es] "Implementacion" step 2, [nl] "Implementatie" step 2)
+
+
+def budget(nb: int, sink_blocks: int, k_min: int, rho0: float, tau: float) -> np.ndarray:
+    """k_i for the nb query blocks of one sequence (int64).
+
+    k_dyn(i) = max(k_min, ceil(rho0 * exp(-i/tau) * (i+1)))   (float64 math)
+    k_i      = i+1                          if i < S
+             = min(i+1, S + 1 + k_dyn(i))   otherwise
+    i is the 0-based block index within the sequence, tau is in blocks and
+    (i+1) counts the causal key blocks of row i."""
+    out = np.zeros(nb, dtype=np.int64)
+    for i in range(nb):
+        if i < sink_blocks:
+            out[i] = i + 1
+            continue
+        x = rho0 * math.exp(-i / tau) * (i + 1)
+        kd = max(k_min, int(math.ceil(x)))
+        out[i] = min(i + 1, sink_blocks + 1 + kd)
+    return out
+
+
+def budget_linear(nb: int, sink_blocks: int, k_start: int, mu: float) -> np.ndarray:
+    """The pages' linear form ([es] 2.A, [fr] 2.A): the number of dynamically
+    chosen blocks goes linearly from k_start at the first query block to
+    mu*k_start at the last, rounded up; sinks and diagonal are added on top."""
+    out = np.zeros(nb, dtype=np.int64)
+    for i in range(nb):
+        if i < sink_blocks:
+            out[i] = i + 1
+            continue
+        frac = 0.0 if nb <= 1 else i / (nb - 1)
+        kd = int(math.ceil(k_start * (1.0 - frac) + mu * k_start * frac))
+        out[i] = min(i + 1, sink_blocks + 1 + max(kd, 0))
+    return out
+
+
+# ----------------------------------------------------------------------------
+# selection: forced sink blocks (initial tokens are recursive anchors, [es] 1,
+# [fr] 1 and 2.A) plus the diagonal, then the top blocks of the metric
+# ([es] "Implementacion" step 3, [nl] "Implementatie" step 3)
+
+
+def _rank_key(values: np.ndarray, idx: np.ndarray) -> np.ndarray:
+    """Order for 'best first': larger metric first, ties to smaller index,
+    NaN last.  Returns a permutation of positions."""
+    v = values.astype(np.float64)
+    nan = np.isnan(v)
+    neg = np.where(nan, 0.0, -v)
+    neg = neg + 0.0          # -0.0 -> +0.0 so that -0 and +0 tie
+    return np.lexsort((idx, neg, nan))
+
+
+def select_row(m_row: np.ndarray, i: int, k_i: int, sink_blocks: int) -> np.ndarray:
+    """Selected key blocks of query block i, ascending (int64).
+
+    forced F = {0..min(S, i+1)-1} U {i}; candidates C = {S..i-1}; the best
+    (k_i - |F|) candidates by m are added (all of them if fewer remain)."""
+    forced = set(range(min(sink_blocks, i + 1)))
+    forced.add(i)
+    cand = np.arange(sink_blocks, i, dtype=np.int64)
+    take = max(0, k_i - len(forced))
+    chosen: List[int] = []
+    if take > 0 and cand.size:
+        order = _rank_key(m_row[cand], cand)
+        chosen = [int(c) for c in cand[order[:take]]]
+    return np.array(sorted(forced | set(chosen)), dtype=np.int64)
+
+
+def select(m: np.ndarray, cu_blocks: np.ndarray, budgets: np.ndarray,
+           sink_blocks: int, kmax: Optional[int] = None):
+    """idx [Hq, nbT, kmax] int32 (-1 padded, ascending, sequence-local block
+    numbers) and count [Hq, nbT] int32.  ``budgets`` is per global block."""
+    Hq = m.shape[0]
+    nbT = int(cu_blocks[-1])
+    if kmax is None:
+        kmax = int(budgets.max()) if nbT else 0
+    idx = np.full((Hq, nbT, kmax), -1, dtype=np.int32)
+    cnt = np.zeros((Hq, nbT), dtype=np.int32)
+    for h in range(Hq):
+        for s in range(len(cu_blocks) - 1):
+            b0 = int(cu_blocks[s])
+            for i in range(int(cu_blocks[s + 1]) - b0):
+                sel = select_row(score_row(m, cu_blocks, h, s, i), i,
+                                 int(budgets[b0 + i]), sink_blocks)
+                idx[h, b0 + i, :sel.size] = sel
+                cnt[h, b0 + i] = sel.size
+    return idx, cnt
+
+
+# ----------------------------------------------------------------------------
+# exact softmax aggregation over the selected blocks only ([es]
+# "Implementacion" step 3, [it] 2.C, [nl] "Implementatie" step 3, [fr] 2.C
+# step 3)
+
+
+def attn_row(q: np.ndarray, k: np.ndarray, v: np.ndarray, cu_seqlens, block: int,
+             s: int, i: int, h: int, G: int, blocks: Iterable[int]):
+    """Output rows and natural-log LSE for the tokens of query block i of
+    sequence s, query head h, attending to the given local key blocks.
+
+    Token-level causality: key token position p may be seen by query token
+    position t iff p <= t (positions are local to the sequence)."""
+    cu = np.asarray(cu_seqlens, dtype=np.int64)
+    a, e = int(cu[s]), int(cu[s + 1])
+    g = h // G
+    t0 = a + i * block
+    t1 = min(t0 + block, e)
+    keys = []
+    for j in blocks:
+        j0 = a + int(j) * block
+        keys.extend(range(j0, min(j0 + block, e)))
+    keys = np.asarray(keys, dtype=np.int64)
+    qi = q[t0:t1, h, :].astype(np.float64)
+    kj = k[keys, g, :].astype(np.float64)
+    vj = v[keys, g, :].astype(np.float64)
+    d = q.shape[2]
+    logits = (qi @ kj.T) / math.sqrt(d)
+    allowed = keys[None, :] <= np.arange(t0, t1)[:, None]
+    logits = np.where(allowed, logits, -np.inf)
+    mx = logits.max(axis=1, keepdims=True)
+    p = np.exp(logits - mx)
+    l = p.sum(axis=1, keepdims=True)
+    o = (p @ vj) / l
+    lse = (mx + np.log(l))[:, 0]
+    return o, lse
+
+
+def sparse_attn(q: np.ndarray, k: np.ndarray, v: np.ndarray, idx: np.ndarray,
+                count: np.ndarray, cu_seqlens, block: int,
+                rows: Optional[Iterable[Tuple[int, int]]] = None):
+    """Block-sparse causal attention.
+
+    Returns (o [T, Hq, d], lse [Hq, T]) in float64 for every row when
+    ``rows`` is None; otherwise a dict {(h, global_block): (o_rows, lse_rows)}
+    for just the requested (query head, global query block) pairs."""
+    T, Hq, d = q.shape
+    G = Hq // k.shape[1]
+    cu = np.asarray(cu_seqlens, dtype=np.int64)
+    cub = block_layout(cu, block)
+    seq_of_block = np.repeat(np.arange(len(cu) - 1), np.diff(cub))
+
+    def one(h, b):
+        s = int(seq_of_block[b])
+        i = b - int(cub[s])
+        blocks = idx[h, b, :int(count[h, b])]
+        return attn_row(q, k, v, cu, block, s, i, h, G, blocks)
+
+    if rows is not None:
+        return {(h, b): one(h, b) for (h, b) in rows}
+    o = np.zeros((T, Hq, d), dtype=np.float64)
+    lse = np.zeros((Hq, T), dtype=np.float64)
+    for h in range(Hq):
+        for b in range(int(cub[-1])):
+            s = int(seq_of_block[b])
+            t0 = int(cu[s]) + (b - int(cub[s])) * block
+            t1 = min(t0 + block, int(cu[s + 1]))
+            ob, lb = one(h, b)
+            o[t0:t1, h, :] = ob
+            lse[h, t0:t1] = lb
+    return o, lse
+
+
+def dense_causal_attn(q: np.ndarray, k: np.ndarray, v: np.ndarray, cu_seqlens):
+    """Ordinary causal softmax attention per sequence, written independently
+    of the block machinery (for the full-budget check).  float64."""
+    T, Hq, d = q.shape
+    G = Hq // k.shape[1]
+    cu = np.asarray(cu_seqlens, dtype=np.int64)
+    o = np.zeros((T, Hq, d), dtype=np.float64)
+    lse = np.zeros((Hq, T), dtype=np.float64)
+    for s in range(len(cu) - 1):
+        a, e = int(cu[s]), int(cu[s + 1])
+        n = e - a
+        if n == 0:
+            continue
+        mask = np.tril(np.ones((n, n), dtype=bool))
+        for h in range(Hq):
+            qq = q[a:e, h, :].astype(np.float64)
+            kk = k[a:e, h // G, :].astype(np.float64)
+            vv = v[a:e, h // G, :].astype(np.float64)
+            lg = np.where(mask, qq @ kk.T / math.sqrt(d), -np.inf)
+            mx = lg.max(axis=1, keepdims=True)
+            p = np.exp(lg - mx)
+            l = p.sum(axis=1, keepdims=True)
+            o[a:e, h, :] = (p @ vv) / l
+            lse[h, a:e] = (mx + np.log(l))[:, 0]
+    return o, lse
+
+
+# ----------------------------------------------------------------------------
+# the whole path
+
+
+def budgets_for(cu_blocks: np.ndarray, sink_blocks: int, k_min: int,
+                rho0: float, tau: float) -> np.ndarray:
+    """Per-global-block budget table, each sequence restarting at i = 0."""
+    parts = [budget(int(cu_blocks[s + 1] - cu_blocks[s]), sink_blocks, k_min, rho0, tau)
+             for s in range(len(cu_blocks) - 1)]
+    return np.concatenate(parts) if parts else np.zeros(0, np.int64)
+
+
+def prefill(q, k, v, cu_seqlens, block, sink_blocks, k_min, rho0, tau,
+            vnorm_mode: str = "mean"):
+    """pool -> score -> budget -> select -> attention.  Returns a dict of
+    every intermediate (float64 / int)."""
+    d = q.shape[2]
+    cub = block_layout(cu_seqlens, block)
+    qbar = pool_mean(q, cu_seqlens, block)
+    kbar = pool_mean(k, cu_seqlens, block)
+    w = pool_vnorm(v, cu_seqlens, block, vnorm_mode)
+    m = score(qbar, kbar, w, cub, d)
+    bud = budgets_for(cub, sink_blocks, k_min, rho0, tau)
+    idx, cnt = select(m, cub, bud, sink_blocks)
+    o, lse = sparse_attn(q, k, v, idx, cnt, cu_seqlens, block)
+    return dict(qbar=qbar, kbar=kbar, w=w, m=m, budget=bud, idx=idx,
+                count=cnt, o=o, lse=lse, cu_blocks=cub)
