@@ -1,0 +1,144 @@
+// Token Position-Decay top-k block selection (gist.science/es
+// "Implementacion" steps 2-3; gist.science/nl "Implementatie" steps 2-3;
+// initial blocks are always kept because every later token aggregates them,
+// gist.science/es section 1 and gist.science/fr section 1).
+//
+// One 64-wide wavefront per (query head, query block) row.  The row's
+// candidate metrics are read once (coalesced) into registers as
+// order-preserving 32-bit keys.  The k-th largest key is found by a 32-step
+// bitwise bisection whose counts come from wavefront ballots (v_cmp straight
+// into a scalar mask, popcount on the scalar unit), so the cost does not
+// depend on k.  Keys above the threshold are kept; keys equal to it are kept
+// in ascending block order until the budget is met, which is exactly "larger
+// metric first, equal metrics to the smaller block number".  The kept blocks
+// are written in ascending order with ballot/mbcnt compaction, after the
+// forced sink blocks and before the forced diagonal block.
+#include "stem_device.h"
+#include "stem_internal.h"
+
+namespace stem {
+namespace {
+
+struct SelectArgs {
+  const float *scores;
+  int32_t *idx, *count;
+  PlanDev pd;
+  int32_t Hq, nbT, kmax, sinks;
+  int64_t per_head;
+};
+
+// Order-preserving key: larger float -> larger key; -0 == +0; NaN -> 1
+// (below every number); 0 is reserved for "not a candidate".
+__device__ __forceinline__ uint32_t order_key(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 1u;
+  if (u == 0x80000000u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
+  return __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(mask >> 32),
+                                   __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(mask), 0u));
+}
+
+template <int E>
+__global__ __launch_bounds__(256) void select_kernel(SelectArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (row >= int64_t(a.Hq) * a.nbT) return;
+  const int h = static_cast<int>(row / a.nbT);
+  const int b = static_cast<int>(row % a.nbT);
+  const int s = a.pd.blk_seq[b];
+  const int i = b - a.pd.cu_blocks[s];
+  const int k_i = a.pd.budget[b];
+  const int S = a.sinks;
+  int32_t *out = a.idx + row * a.kmax;
+  if (lane == 0) a.count[row] = k_i;
+
+  const int nforced = i < S ? i + 1 : S + 1;
+  const int ncand = i < S ? 0 : i - S;
+  const int take = k_i - nforced;
+  if (take >= ncand) {  // every causal block is kept
+    for (int p = lane; p < a.kmax; p += 64) out[p] = p <= i ? p : -1;
+    return;
+  }
+  const float *mrow = a.scores + int64_t(h) * a.per_head + a.pd.tri[s] +
+                      (int64_t(i) * (i + 1)) / 2;
+  uint32_t key[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int j = S + lane + 64 * e;
+    key[e] = j < i ? order_key(mrow[j]) : 0u;
+  }
+  // largest T with #{key >= T} >= take (take >= 1 here, and all
+  // candidates have key >= 1, so T >= 1 and padding never qualifies)
+  uint32_t T = 0;
+  if (take > 0) {
+    for (int bit = 31; bit >= 0; --bit) {
+      const uint32_t cand = T | (1u << bit);
+      int cnt = 0;
+#pragma unroll
+      for (int e = 0; e < E; ++e) cnt += __popcll(__ballot(key[e] >= cand));
+      if (cnt >= take) T = cand;
+    }
+  } else {
+    T = 0xffffffffu;  // nothing to take: no key passes "> T", none ties
+  }
+  int gt = 0;
+#pragma unroll
+  for (int e = 0; e < E; ++e) gt += __popcll(__ballot(key[e] > T));
+  const int need_eq = take > 0 ? take - gt : 0;
+
+  int pos = S, eq_seen = 0;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const bool is_eq = take > 0 && key[e] == T;
+    const uint64_t eqm = __ballot(is_eq);
+    const int rank = eq_seen + static_cast<int>(lanes_below(eqm));
+    eq_seen += __popcll(eqm);
+    const bool sel = key[e] > T || (is_eq && rank < need_eq);
+    const uint64_t sm = __ballot(sel);
+    if (sel) out[pos + static_cast<int>(lanes_below(sm))] = S + lane + 64 * e;
+    pos += __popcll(sm);
+  }
+  for (int p = lane; p < S; p += 64) out[p] = p;
+  if (lane == 0) out[S + take] = i;
+  for (int p = S + take + 1 + lane; p < a.kmax; p += 64) out[p] = -1;
+}
+
+}  // namespace
+
+hipError_t launch_select(const stem_plan_info &in, PlanDev pd, const float *scores,
+                         int32_t *idx, int32_t *count, hipStream_t st) {
+  const int64_t rows = int64_t(in.num_q_heads) * in.total_blocks;
+  if (rows == 0) return hipSuccess;
+  SelectArgs a;
+  a.scores = scores; a.idx = idx; a.count = count;
+  a.pd = pd;
+  a.Hq = in.num_q_heads;
+  a.nbT = static_cast<int32_t>(in.total_blocks);
+  a.kmax = in.kmax;
+  a.sinks = in.sink_blocks;
+  a.per_head = in.score_elems_per_head;
+  const dim3 grid(static_cast<unsigned>((rows + 3) / 4));
+  const int ncand = in.max_seq_blocks;  // upper bound of candidates per row
+  if (ncand <= 64)
+    hipLaunchKernelGGL((select_kernel<1>), grid, dim3(256), 0, st, a);
+  else if (ncand <= 128)
+    hipLaunchKernelGGL((select_kernel<2>), grid, dim3(256), 0, st, a);
+  else if (ncand <= 256)
+    hipLaunchKernelGGL((select_kernel<4>), grid, dim3(256), 0, st, a);
+  else if (ncand <= 512)
+    hipLaunchKernelGGL((select_kernel<8>), grid, dim3(256), 0, st, a);
+  else if (ncand <= 1024)
+    hipLaunchKernelGGL((select_kernel<16>), grid, dim3(256), 0, st, a);
+  else if (ncand <= 2048)
+    hipLaunchKernelGGL((select_kernel<32>), grid, dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL((select_kernel<64>), grid, dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+static_assert(STEM_MAX_SEQ_BLOCKS <= 64 * 64, "select keeps <= 64 keys per lane");
+
+}  // namespace stem

@@ -1,0 +1,71 @@
+// Device-side helpers and the launch interface between the C entry points
+// (stem_api.hip) and the kernels (pool.hip, score.hip, select.hip,
+// attn.hip).  gfx950 (CDNA4) only: 64-wide wavefronts, MFMA matrix cores.
+#ifndef STEM_DEVICE_H
+#define STEM_DEVICE_H
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "stem.h"
+
+namespace stem {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Plan arrays on the device (see stem_plan_info for their meaning).
+struct PlanDev {
+  const int32_t *cu_seqlens;
+  const int32_t *cu_blocks;
+  const int64_t *tri;
+  const int32_t *blk_seq;
+  const int32_t *budget;
+  const int32_t *order;
+};
+
+inline PlanDev make_plan_dev(const stem_plan_info &in, const void *base) {
+  const char *b = static_cast<const char *>(base);
+  PlanDev p;
+  p.cu_seqlens = reinterpret_cast<const int32_t *>(b + in.off_cu_seqlens);
+  p.cu_blocks = reinterpret_cast<const int32_t *>(b + in.off_cu_blocks);
+  p.tri = reinterpret_cast<const int64_t *>(b + in.off_tri);
+  p.blk_seq = reinterpret_cast<const int32_t *>(b + in.off_blk_seq);
+  p.budget = reinterpret_cast<const int32_t *>(b + in.off_budget);
+  p.order = reinterpret_cast<const int32_t *>(b + in.off_order);
+  return p;
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
+  return __uint_as_float(bits16 << 16);
+}
+
+// Round-to-nearest-even float -> bf16 bits (finite inputs; NaN stays NaN).
+__device__ __forceinline__ uint16_t f32_to_bf16(float x) {
+  __bf16 h = static_cast<__bf16>(x);
+  return __builtin_bit_cast(uint16_t, h);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return uint32_t(f32_to_bf16(lo)) | (uint32_t(f32_to_bf16(hi)) << 16);
+}
+
+// Launchers (return hipSuccess or the launch error).
+hipError_t launch_pool(const stem_plan_info &in, PlanDev pd, const void *q,
+                       const void *k, const void *v, float *qbar, float *kbar,
+                       float *vnorm, int vnorm_mode, hipStream_t st);
+hipError_t launch_score(const stem_plan_info &in, PlanDev pd, const float *qbar,
+                        const float *kbar, const float *vnorm, float *scores,
+                        hipStream_t st);
+hipError_t launch_select(const stem_plan_info &in, PlanDev pd, const float *scores,
+                         int32_t *idx, int32_t *count, hipStream_t st);
+hipError_t launch_attn(const stem_plan_info &in, PlanDev pd, const void *q,
+                       const void *k, const void *v, const int32_t *idx,
+                       const int32_t *count, void *out, int out_dtype, float *lse,
+                       hipStream_t st);
+
+}  // namespace stem
+
+#endif

@@ -140,23 +140,28 @@ def score(qbar: np.ndarray, kbar: np.ndarray, w: np.ndarray,
         m_ij = p_ij * w_j
     """
     Hq = qbar.shape[0]
-    Hkv = kbar.shape[0]
-    G = Hq // Hkv
     offs, total = score_offsets(cu_blocks)
     out = np.zeros((Hq, total), dtype=np.float64)
-    scale = 1.0 / math.sqrt(head_dim)
     for h in range(Hq):
-        g = h // G
         for s in range(len(cu_blocks) - 1):
-            b0 = int(cu_blocks[s])
-            nb = int(cu_blocks[s + 1]) - b0
+            nb = int(cu_blocks[s + 1]) - int(cu_blocks[s])
             for i in range(nb):
-                logits = kbar[g, b0:b0 + i + 1, :] @ qbar[h, b0 + i, :] * scale
-                p = np.exp(logits - logits.max())
-                p /= p.sum()
                 row0 = int(offs[s]) + tri(i)
-                out[h, row0:row0 + i + 1] = p * w[g, b0:b0 + i + 1]
+                out[h, row0:row0 + i + 1] = score_row_values(qbar, kbar, w, cu_blocks,
+                                                             head_dim, h, s, i)
     return out
+
+
+def score_row_values(qbar: np.ndarray, kbar: np.ndarray, w: np.ndarray,
+                     cu_blocks: np.ndarray, head_dim: int, h: int, s: int, i: int) -> np.ndarray:
+    """One row of the metric: m_i0 .. m_ii for query head h, sequence s,
+    local query block i (see score)."""
+    g = h // (qbar.shape[0] // kbar.shape[0])
+    b0 = int(cu_blocks[s])
+    logits = kbar[g, b0:b0 + i + 1, :] @ qbar[h, b0 + i, :] * (1.0 / math.sqrt(head_dim))
+    p = np.exp(logits - logits.max())
+    p /= p.sum()
+    return p * w[g, b0:b0 + i + 1]
 
 
 def score_row(m: np.ndarray, cu_blocks: np.ndarray, h: int, s: int, i: int) -> np.ndarray:

@@ -1,0 +1,148 @@
+"""Shared helpers of the GPU parity tests: run the HIP path through the C ABI
+and compare with the oracle.  Tolerances (absolute, max over elements):
+
+  * bf16 inputs: 2e-2 on scores and on the f32 attention output; the bf16
+    output is allowed 2e-2 plus half a bf16 ulp of the reference value
+    (rounding the output to bf16 alone costs up to half an ulp, which
+    exceeds 2e-2 once |o| >= 8).  Scores must also match to 1e-4 relative:
+    both paths read identical bf16 values and differ only in summation order
+    and f32 vs f64 arithmetic.
+  * f32 inputs: 1e-5 on scores and outputs.
+  * block selection: bit-exact when both sides rank the same score array.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+from block_sparse_causal_amd import stem
+from block_sparse_causal_amd import synthetic as syn
+from oracle import stem_oracle as O
+
+TOL = {"bf16": dict(score=2e-2, score_rel=1e-4, out=2e-2, lse=2e-3, pool=2e-5),
+       "f32": dict(score=1e-5, score_rel=1e-5, out=1e-5, lse=1e-5, pool=1e-5)}
+
+
+def log(msg: str) -> None:
+    print(msg, flush=True)
+
+
+def upload(x: syn.Inputs, device="cuda"):
+    import torch
+    if x.workload.dtype == "bf16":
+        conv = lambda b: torch.from_numpy(b.view(np.int16)).to(device).view(torch.bfloat16)
+        return conv(x.q_bits), conv(x.k_bits), conv(x.v_bits)
+    return tuple(torch.from_numpy(a).to(device) for a in (x.q, x.k, x.v))
+
+
+class GpuRun:
+    """Plan, upload and run the whole path once; keep host copies."""
+
+    def __init__(self, w: syn.Workload, x: syn.Inputs = None, out_dtype="f32", vnorm_mode=0,
+                 plan_override=None):
+        import torch
+        self.w = w
+        self.x = x if x is not None else syn.generate(w)
+        self.plan = stem.plan_for(w, **(plan_override or {})).to("cuda")
+        q, k, v = upload(self.x)
+        odt = torch.float32 if out_dtype == "f32" else torch.bfloat16
+        b = stem.prefill(self.plan, q, k, v, out_dtype=odt, vnorm_mode=vnorm_mode)
+        torch.cuda.synchronize()
+        self.qbar = b.qbar.cpu().numpy()
+        self.kbar = b.kbar.cpu().numpy()
+        self.vnorm = b.vnorm.cpu().numpy()
+        self.scores = b.scores.cpu().numpy()
+        self.idx = b.idx.cpu().numpy()
+        self.count = b.count.cpu().numpy()
+        self.out = b.out.float().cpu().numpy()
+        self.lse = b.lse.cpu().numpy()
+        self.out_dtype = out_dtype
+        self.cu_blocks = np.asarray(self.plan.cu_blocks, dtype=np.int64)
+        self.budget = np.asarray(self.plan.budget, dtype=np.int64)
+        del b, q, k, v
+
+
+def bf16_half_ulp(x: np.ndarray) -> np.ndarray:
+    ax = np.maximum(np.abs(x), np.finfo(np.float32).tiny)
+    e = np.floor(np.log2(ax))
+    return np.exp2(e - 8)  # a bf16 ulp at |x| is 2^(e-7); half of it is 2^(e-8)
+
+
+def check_out(got: np.ndarray, ref: np.ndarray, dtype: str, out_dtype: str, what: str):
+    tol = TOL[dtype]["out"]
+    err = np.abs(got - ref)
+    if out_dtype == "bf16":
+        bound = tol + bf16_half_ulp(ref)
+    else:
+        bound = np.full_like(ref, tol)
+    bad = err > bound
+    assert not bad.any(), (f"{what}: {int(bad.sum())} elements out of tolerance, max err "
+                           f"{err.max():.3g} (bound {tol})")
+    return float(err.max())
+
+
+def check_scores(got: np.ndarray, ref: np.ndarray, dtype: str, what: str):
+    t = TOL[dtype]
+    err = np.abs(got - ref)
+    assert err.max() <= t["score"], f"{what}: max abs err {err.max():.3g}"
+    rel = err / np.maximum(np.abs(ref), 1e-30)
+    assert rel.max() <= t["score_rel"], f"{what}: max rel err {rel.max():.3g}"
+    return float(err.max()), float(rel.max())
+
+
+def select_rows_crossfed(r: GpuRun, rows):
+    """Oracle selection on the GPU's own scores must equal the GPU's lists."""
+    offs, _ = O.score_offsets(r.cu_blocks)
+    seq_of = np.repeat(np.arange(len(r.cu_blocks) - 1), np.diff(r.cu_blocks))
+    S = r.w.sink_blocks
+    for (h, b) in rows:
+        s = int(seq_of[b]); i = b - int(r.cu_blocks[s])
+        row0 = int(offs[s]) + O.tri(i)
+        m = r.scores[h, row0:row0 + i + 1].astype(np.float64)
+        want = O.select_row(m, i, int(r.budget[b]), S)
+        n = int(r.count[h, b])
+        assert n == want.size, (h, b, n, want.size)
+        got = r.idx[h, b, :n]
+        assert np.array_equal(got, want), (h, b, got, want)
+        assert np.all(r.idx[h, b, n:] == -1), (h, b)
+
+
+def attn_rows_crossfed(r: GpuRun, rows, what="attn"):
+    """Oracle attention with the GPU's block lists, on sampled rows."""
+    res = O.sparse_attn(r.x.q, r.x.k, r.x.v, r.idx, r.count, r.w.cu_seqlens, r.w.block,
+                        rows=rows)
+    cu = r.w.cu_seqlens
+    seq_of = np.repeat(np.arange(len(r.cu_blocks) - 1), np.diff(r.cu_blocks))
+    worst = 0.0
+    lse_worst = 0.0
+    for (h, b), (o, l) in res.items():
+        s = int(seq_of[b]); i = b - int(r.cu_blocks[s])
+        t0 = int(cu[s]) + i * r.w.block
+        t1 = t0 + o.shape[0]
+        worst = max(worst, check_out(r.out[t0:t1, h], o, r.w.dtype, r.out_dtype, f"{what} {(h, b)}"))
+        le = np.abs(r.lse[h, t0:t1] - l).max()
+        assert le <= TOL[r.w.dtype]["lse"], f"{what} lse {(h, b)}: {le}"
+        lse_worst = max(lse_worst, float(le))
+    return worst, lse_worst
+
+
+def all_rows(r: GpuRun):
+    return [(h, b) for h in range(r.w.num_q_heads) for b in range(int(r.cu_blocks[-1]))]
+
+
+def sample_rows(r: GpuRun, n: int, seed: int = 0):
+    """First, last and diagonal-interesting rows plus a random sample."""
+    rng = np.random.default_rng(seed)
+    nbT = int(r.cu_blocks[-1])
+    Hq = r.w.num_q_heads
+    rows = set()
+    for s in range(len(r.cu_blocks) - 1):
+        b0, b1 = int(r.cu_blocks[s]), int(r.cu_blocks[s + 1])
+        for b in {b0, b0 + 1, b0 + 2, b1 - 1}:
+            if b0 <= b < b1:
+                rows.add((int(rng.integers(Hq)), b))
+                rows.add((Hq - 1, b))
+    while len(rows) < n and len(rows) < Hq * nbT:
+        rows.add((int(rng.integers(Hq)), int(rng.integers(nbT))))
+    return sorted(rows)

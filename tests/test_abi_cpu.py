@@ -1,0 +1,143 @@
+"""Host-side checks of libstem that need no GPU: the library loads and exports
+every entry point the header declares, stem_plan agrees with the oracle's
+layout and budget tables exactly, and bad arguments are rejected before any
+HIP call."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from block_sparse_causal_amd import stem
+from block_sparse_causal_amd import synthetic as syn
+from oracle import stem_oracle as O
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_library_exports_every_declared_symbol():
+    hdr = open(os.path.join(ROOT, "include", "stem.h")).read()
+    names = set(re.findall(r"^\s*(?:int|const char \*)\s*(stem_\w+)\s*\(", hdr, re.M))
+    assert names >= {"stem_plan", "stem_pool", "stem_score", "stem_select",
+                     "stem_sparse_attn", "stem_status_str"}
+    L = stem.lib()
+    for n in sorted(names):
+        assert hasattr(L, n), n
+    # the binding uses the same names
+    for n in names - {"stem_status_str"}:
+        assert hasattr(stem, n), n
+
+
+def test_struct_layouts_match_header():
+    # offsets follow C layout rules; a mismatch would corrupt every call
+    assert ctypes.sizeof(stem.stem_params) == 24
+    assert stem.stem_plan_info.total_tokens.offset == 40
+    assert ctypes.sizeof(stem.stem_plan_info) == 40 + 11 * 8
+    assert stem.stem_problem.cu_seqlens.offset == 8
+
+
+@pytest.mark.parametrize("name", list(syn.WORKLOADS))
+def test_plan_matches_oracle_tables(name):
+    w = syn.WORKLOADS[name]
+    p = stem.plan_for(w)
+    cub = O.block_layout(w.cu_seqlens, w.block)
+    bud = O.budgets_for(cub, w.sink_blocks, w.k_min, w.rho0, w.tau)
+    offs, total = O.score_offsets(cub)
+    np.testing.assert_array_equal(p.cu_blocks, cub)
+    np.testing.assert_array_equal(p.budget, bud)
+    np.testing.assert_array_equal(p.tri, offs)
+    assert p.info.score_elems_per_head == total
+    assert p.info.total_blocks == cub[-1]
+    assert p.info.kmax == bud.max()
+    assert p.info.executed_blocks_per_head == bud.sum()
+    np.testing.assert_array_equal(p.blk_seq, np.repeat(np.arange(len(w.seqlens)), np.diff(cub)))
+    assert sorted(p.order.tolist()) == list(range(int(cub[-1])))
+
+
+@pytest.mark.parametrize("seed", range(20))
+def test_plan_budget_random_parameters(seed):
+    r = np.random.default_rng(seed)
+    seqlens = list(r.integers(0, 3000, size=r.integers(1, 5)))
+    block = int(r.choice([64, 128]))
+    S = int(r.integers(0, 5))
+    k_min = int(r.integers(0, 12))
+    rho0 = float(r.choice([0.0, r.uniform(0, 2), 1.0, 0.5]))
+    tau = float(r.choice([r.uniform(0.5, 300), 64.0, 1e9]))
+    cu = np.concatenate([[0], np.cumsum(seqlens)])
+    p = stem.stem_plan(cu, 4, 2, 64, block, "bf16", S, k_min, rho0, tau)
+    cub = O.block_layout(cu, block)
+    np.testing.assert_array_equal(p.budget, O.budgets_for(cub, S, k_min, rho0, tau))
+
+
+def test_plan_ragged_and_empty_sequences():
+    cu = [0, 0, 1, 1, 130, 130]
+    p = stem.stem_plan(cu, 2, 1, 64, 64, "f32", 1, 1, 0.5, 4.0)
+    assert list(p.cu_blocks) == [0, 0, 1, 1, 4, 4]
+    assert p.info.total_tokens == 130
+    assert list(p.blk_seq) == [1, 3, 3, 3]
+
+
+def _status(fn, *args):
+    with pytest.raises(stem.StemError) as e:
+        fn(*args)
+    return e.value.status
+
+
+def test_plan_rejects_bad_arguments():
+    ok = dict(cu_seqlens=[0, 128], num_q_heads=4, num_kv_heads=2, head_dim=64, block=64,
+              dtype="bf16", sink_blocks=1, k_min=1, rho0=0.5, tau=4.0)
+
+    def bad(**kw):
+        a = dict(ok); a.update(kw)
+        return _status(stem.stem_plan, *a.values())
+
+    assert bad(num_kv_heads=3) == stem.STEM_EINVAL
+    assert bad(num_q_heads=0) == stem.STEM_EINVAL
+    assert bad(head_dim=96) == stem.STEM_EUNSUPPORTED
+    assert bad(block=32) == stem.STEM_EUNSUPPORTED
+    assert bad(dtype="f16") == stem.STEM_EUNSUPPORTED
+    assert bad(cu_seqlens=[1, 128]) == stem.STEM_EINVAL
+    assert bad(cu_seqlens=[0, 128, 64]) == stem.STEM_EINVAL
+    assert bad(sink_blocks=-1) == stem.STEM_EINVAL
+    assert bad(k_min=-1) == stem.STEM_EINVAL
+    assert bad(rho0=-0.1) == stem.STEM_EINVAL
+    assert bad(rho0=float("nan")) == stem.STEM_EINVAL
+    assert bad(tau=0.0) == stem.STEM_EINVAL
+    assert bad(tau=float("inf")) == stem.STEM_EINVAL
+    assert bad(cu_seqlens=[0, 64 * 4097]) == stem.STEM_EUNSUPPORTED
+
+
+def test_plan_reports_small_buffer():
+    L = stem.lib()
+    cu = np.array([0, 1000], dtype=np.int32)
+    pr = stem.stem_problem(1, cu.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), 2, 1, 64, 64, 1)
+    pa = stem.stem_params(1, 2, 0.5, 4.0)
+    info = stem.stem_plan_info()
+    assert L.stem_plan(ctypes.byref(pr), ctypes.byref(pa), ctypes.byref(info), None, 0) == 0
+    buf = np.zeros(int(info.plan_bytes) - 1, dtype=np.uint8)
+    assert L.stem_plan(ctypes.byref(pr), ctypes.byref(pa), ctypes.byref(info),
+                       buf.ctypes.data, buf.nbytes) == stem.STEM_ESPACE
+
+
+def test_device_calls_reject_bad_arguments_before_any_launch():
+    # these return before touching the HIP runtime, so they run without a GPU
+    L = stem.lib()
+    p = stem.plan_for(syn.custom([256], 4, 2, 64, "bf16", 64))
+    info = p.info
+    P = 1 << 20  # a fake, 16-byte aligned address: never dereferenced
+    assert L.stem_pool(None, P, P, P, P, P, P, P, 0, None) == stem.STEM_EINVAL
+    assert L.stem_pool(ctypes.byref(info), None, P, P, P, P, P, P, 0, None) == stem.STEM_EINVAL
+    assert L.stem_pool(ctypes.byref(info), P, None, P, P, P, P, P, 0, None) == stem.STEM_EINVAL
+    assert L.stem_pool(ctypes.byref(info), P, P + 2, P, P, P, P, P, 0, None) == stem.STEM_EINVAL
+    assert L.stem_pool(ctypes.byref(info), P, P, P, P, P, P, P, 7, None) == stem.STEM_EINVAL
+    assert L.stem_score(ctypes.byref(info), P, P, P, P, None, None) == stem.STEM_EINVAL
+    assert L.stem_select(ctypes.byref(info), P, P, P, None, None) == stem.STEM_EINVAL
+    assert L.stem_sparse_attn(ctypes.byref(info), P, P, P, P, P, P, P, 5, None, None) == \
+        stem.STEM_EUNSUPPORTED
+    assert L.stem_sparse_attn(ctypes.byref(info), P, P, P, P, P, P, P + 4, 0, None, None) == \
+        stem.STEM_EINVAL
+    bad = stem.stem_plan_info.from_buffer_copy(info)
+    bad.magic = 0
+    assert L.stem_score(ctypes.byref(bad), P, P, P, P, P, None) == stem.STEM_EINVAL
+    assert stem.status_str(stem.STEM_EUNSUPPORTED) == "unsupported configuration"
