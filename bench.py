@@ -1,0 +1,261 @@
+"""Benchmark of the Stem sparse-prefill path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one pass of the whole path over one batch of synthetic input with
+the inputs already resident in HBM: stem_pool -> stem_score -> stem_select
+-> stem_sparse_attn, all through the C ABI on one stream.  Each call is
+bracketed by HIP events on that stream, so per-stage times (and the
+attention kernel's own duration, used for the roofline) are measured live.
+
+Reported (one JSON line on stdout, progress on stderr):
+  value       prefill latency per step in ms (the metric is a latency)
+  roofline    the attention kernel against the bf16 matrix-core peak, with
+              algorithmic FLOPs = 4 B^2 d per executed (head, query block,
+              key block), the diagonal block counted as half a tile
+  stages      per-stage ms; effective TFLOP/s of attention and of the step
+  dense       the same attention kernel with every causal block kept (the
+              dense causal comparator) and the speed-up over it
+  cpu_baseline  the CPU oracle timed on a bounded sample and scaled up
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = ("Stem prefill latency (ms) + effective TFLOP/s & % MFMA peak at 128K, "
+          "Llama-8B head shape")
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 matrix-core peak
+PEAK_F32_TFLOPS = 157.3       # MI355X dense f32 matrix-core peak
+PEAK_HBM_GBS = 8000.0
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def attn_flops(plan, diag_half: bool) -> float:
+    i = plan.info
+    per_tile = 4.0 * i.block * i.block * i.head_dim
+    full = per_tile * i.executed_blocks_per_head * i.num_q_heads
+    if not diag_half:
+        return full
+    return full - 0.5 * per_tile * i.total_blocks * i.num_q_heads
+
+
+def upload(x, device="cuda"):
+    import torch
+    if x.workload.dtype == "bf16":
+        conv = lambda b: torch.from_numpy(b.view(np.int16)).to(device).view(torch.bfloat16)
+        return conv(x.q_bits), conv(x.k_bits), conv(x.v_bits)
+    return tuple(torch.from_numpy(a).to(device) for a in (x.q, x.k, x.v))
+
+
+def time_path(plan, q, k, v, bufs, steps: int, warmup: int, vnorm_mode=0):
+    """Run warmup + timed steps; return (ms_per_step wall, per-stage ms lists)."""
+    import torch
+    from block_sparse_causal_amd import stem
+    st = torch.cuda.current_stream()
+    calls = [
+        lambda: stem.stem_pool(plan, q, k, v, bufs.qbar, bufs.kbar, bufs.vnorm, vnorm_mode, st),
+        lambda: stem.stem_score(plan, bufs.qbar, bufs.kbar, bufs.vnorm, bufs.scores, st),
+        lambda: stem.stem_select(plan, bufs.scores, bufs.idx, bufs.count, st),
+        lambda: stem.stem_sparse_attn(plan, q, k, v, bufs.idx, bufs.count, bufs.out, bufs.lse, st),
+    ]
+    for _ in range(warmup):
+        for c in calls:
+            c()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)]
+          for _ in range(steps)]
+    t0 = time.perf_counter()
+    for s in range(steps):
+        ev[s][0].record(st)
+        for n, c in enumerate(calls):
+            c()
+            ev[s][n + 1].record(st)
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) * 1e3 / max(steps, 1)
+    stage = [[ev[s][n].elapsed_time(ev[s][n + 1]) for s in range(steps)] for n in range(len(calls))]
+    total = [ev[s][0].elapsed_time(ev[s][len(calls)]) for s in range(steps)]
+    return wall, stage, total
+
+
+def dense_attention_ms(w, q, k, v, reps: int):
+    """The same attention kernel with every causal block kept."""
+    import torch
+    from block_sparse_causal_amd import stem
+    plan = stem.plan_for(w, k_min=1 << 30, rho0=0.0).to(q.device)
+    bufs = stem.Buffers(plan, q.device, out_dtype=torch.bfloat16)
+    stem.stem_pool(plan, q, k, v, bufs.qbar, bufs.kbar, bufs.vnorm)
+    stem.stem_score(plan, bufs.qbar, bufs.kbar, bufs.vnorm, bufs.scores)
+    stem.stem_select(plan, bufs.scores, bufs.idx, bufs.count)
+    st = torch.cuda.current_stream()
+    stem.stem_sparse_attn(plan, q, k, v, bufs.idx, bufs.count, bufs.out, bufs.lse, st)
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(st)
+        stem.stem_sparse_attn(plan, q, k, v, bufs.idx, bufs.count, bufs.out, bufs.lse, st)
+        b.record(st)
+        torch.cuda.synchronize()
+        times.append(a.elapsed_time(b))
+    flops = attn_flops(plan, diag_half=True)
+    del bufs
+    return float(np.median(times)), flops
+
+
+def cpu_baseline(w, x):
+    """Time the oracle, as it stands, on one KV-head group (KV head 0 and its
+    G query heads: pooling, every metric, selection and attention row of
+    those heads) and scale to all KV heads."""
+    from oracle import stem_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        blas_threads = 1
+    G = w.num_q_heads // w.num_kv_heads
+    q, k, v = x.q[:, :G], x.k[:, :1], x.v[:, :1]
+    t = time.perf_counter()
+    res = O.prefill(q, k, v, w.cu_seqlens, w.block, w.sink_blocks, w.k_min, w.rho0, w.tau)
+    sec = time.perf_counter() - t
+    nbT = int(res["cu_blocks"][-1])
+    sample = (f"oracle prefill of KV head 0 and its {G} query heads of {w.name} "
+              f"(pool, metric, budget, selection and attention of all {nbT} query blocks), "
+              f"scaled by {w.num_kv_heads} KV heads")
+    return dict(value=round(sec * w.num_kv_heads * 1e3, 1), unit="ms", cores=int(blas_threads),
+                kind="oracle", sample=sample, sample_seconds=round(sec, 2),
+                host_cpus=len(os.sched_getaffinity(0)))
+
+
+def copy_calibration(nbytes: int = 1 << 30):
+    """One device-to-device copy of a known size, for scaling the hardware
+    byte counters of a profiling run (its kernel reads and writes nbytes)."""
+    import torch
+    a = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    b.copy_(a)
+    torch.cuda.synchronize()
+    log(f"copy calibration: {nbytes} bytes read and written")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default=None)
+    ap.add_argument("--dense-reps", type=int, default=3)
+    ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from block_sparse_causal_amd import stem
+    from block_sparse_causal_amd import synthetic as syn
+
+    name = args.workload or syn.HEADLINE
+    w = syn.WORKLOADS[name]
+    log(f"workload {name}: generating seeded inputs")
+    t = time.perf_counter()
+    x = syn.generate(w)
+    log(f"inputs ready in {time.perf_counter() - t:.1f}s; uploading")
+    q, k, v = upload(x)
+    plan = stem.plan_for(w).to("cuda")
+    out_dtype = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    bufs = stem.Buffers(plan, "cuda", out_dtype=out_dtype)
+    torch.cuda.synchronize()
+
+    log(f"timing {args.warmup} warmup + {args.steps} steps")
+    wall_ms, stage, total = time_path(plan, q, k, v, bufs, args.steps, args.warmup)
+    names = ["pool", "score", "select", "attn"]
+    stage_ms = {n: float(np.mean(s)) for n, s in zip(names, stage)}
+    step_ms = float(np.mean(total))
+    log(f"step {step_ms:.3f} ms (wall {wall_ms:.3f} ms): " +
+        ", ".join(f"{n} {stage_ms[n]:.3f}" for n in names))
+
+    flops_alg = attn_flops(plan, diag_half=True)
+    flops_full = attn_flops(plan, diag_half=False)
+    attn_ms = stage_ms["attn"]
+    achieved = flops_alg / (attn_ms * 1e-3) / 1e12
+    peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
+    i = plan.info
+    esz = 2 if w.dtype == "bf16" else 4
+    pool_bytes = i.total_tokens * (i.num_q_heads + 2 * i.num_kv_heads) * i.head_dim * esz + \
+        4 * i.total_blocks * ((i.num_q_heads + i.num_kv_heads) * i.head_dim + i.num_kv_heads)
+    select_bytes = 4 * i.num_q_heads * i.score_elems_per_head + \
+        4 * i.num_q_heads * i.total_blocks * (i.kmax + 1)
+
+    result = {
+        "metric": METRIC,
+        "value": round(step_ms, 4),
+        "unit": "ms",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 4),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded; Q,K ~ N(0,1) with RoPE, sink K x3, V ~ N(0,1) x LogNormal(0,0.5))",
+        "config": {"workload": name, "seq_lens": list(w.seqlens), "q_heads": w.num_q_heads,
+                   "kv_heads": w.num_kv_heads, "head_dim": w.head_dim, "block": w.block,
+                   "sink_blocks": w.sink_blocks, "k_min": w.k_min, "rho0": w.rho0,
+                   "tau_blocks": w.tau, "out_dtype": str(out_dtype).replace("torch.", ""),
+                   "executed_blocks_per_head": i.executed_blocks_per_head},
+        "roofline": {"bound": "mfma", "kernel": "attn", "achieved": round(achieved, 2),
+                     "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+                     "traffic": None,
+                     "flop_per_launch": flops_alg,
+                     "avg_launch_ms": round(attn_ms, 4)},
+        "stages_ms": {n: round(stage_ms[n], 4) for n in names},
+        "effective_tflops": {"attn_diag_half": round(achieved, 2),
+                             "attn_full_tiles": round(flops_full / (attn_ms * 1e-3) / 1e12, 2),
+                             "step_diag_half": round(flops_alg / (step_ms * 1e-3) / 1e12, 2)},
+        "hbm_gbs": {"pool": round(pool_bytes / (stage_ms["pool"] * 1e-3) / 1e9, 1),
+                    "select": round(select_bytes / (stage_ms["select"] * 1e-3) / 1e9, 1),
+                    "peak": PEAK_HBM_GBS},
+        "wall_ms_per_step": round(wall_ms, 4),
+    }
+    del bufs
+
+    if not args.no_dense:
+        log("dense comparator: same kernel, every causal block kept")
+        dms, dflops = dense_attention_ms(w, q, k, v, args.dense_reps)
+        result["dense"] = {"attn_ms": round(dms, 3),
+                           "tflops": round(dflops / (dms * 1e-3) / 1e12, 2),
+                           "speedup_vs_stem_step": round(dms / step_ms, 2)}
+        log(f"dense attention {dms:.2f} ms -> speed-up {dms / step_ms:.2f}x")
+
+    if args.copy_calibration:
+        copy_calibration()
+
+    if not args.no_cpu:
+        log("CPU oracle baseline on a bounded sample")
+        result["cpu_baseline"] = cpu_baseline(w, x)
+        log(f"cpu baseline {result['cpu_baseline']['value']} ms (scaled)")
+
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

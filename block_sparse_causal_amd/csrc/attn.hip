@@ -32,6 +32,7 @@ namespace stem {
 namespace {
 
 constexpr int kXcds = 8;
+constexpr float kRescaleLog2 = 8.0f;  // lazy-rescale threshold, log2 units
 
 struct AttnArgs {
   const void *q, *k, *v;
@@ -77,13 +78,16 @@ __device__ __forceinline__ bool decode_item(const AttnArgs &a, Row &r) {
 // ---------------------------------------------------------------------------
 // bf16 inputs
 
+// Two wavefronts per SIMD: while one runs softmax on the vector ALU the other
+// keeps the matrix cores busy, and one workgroup's global loads overlap the
+// other's compute.  That caps a wavefront at 256 registers.
 template <int B, int D, bool OUT_BF16>
-__global__ __launch_bounds__(B * 2) void attn_bf16_kernel(AttnArgs a) {
+__global__ __launch_bounds__(B * 2) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void attn_bf16_kernel(AttnArgs a) {
   constexpr int NW = B / 32;           // wavefronts
   constexpr int NT = NW * 64;          // threads
   constexpr int LDK = D + 8;           // K row stride in LDS (bf16 elements)
   constexpr int LDV = B + 2;           // V^T row stride in LDS (bf16 elements)
-  constexpr int KT = B / 32;           // 32-key sub-tiles per block
   constexpr int DT = D / 32;           // 32-dim output tiles
   constexpr int DC = D / 16;           // 16-dim contraction chunks for S
   __shared__ __attribute__((aligned(16))) uint16_t Ks[B * LDK];
@@ -160,77 +164,86 @@ __global__ __launch_bounds__(B * 2) void attn_bf16_kernel(AttnArgs a) {
     }
     __syncthreads();
 
-    // ---- S^T = K Q^T
-    f32x16 sacc[KT];
+    // ---- the key block in chunks of 64 keys (two 32-key sub-tiles)
 #pragma unroll
-    for (int kt = 0; kt < KT; ++kt) sacc[kt] = f32x16{};
+    for (int kc = 0; kc < B / 64; ++kc) {
+      // S^T = K Q^T for this chunk
+      f32x16 sacc[2];
+      sacc[0] = f32x16{};
+      sacc[1] = f32x16{};
 #pragma unroll
-    for (int c = 0; c < DC; ++c) {
+      for (int c = 0; c < DC; ++c) {
 #pragma unroll
-      for (int kt = 0; kt < KT; ++kt) {
-        const u32x4 kx = *reinterpret_cast<const u32x4 *>(&Ks[(kt * 32 + n) * LDK + c * 16 + hi * 8]);
-        sacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kx), qf[c],
-                                                           sacc[kt], 0, 0, 0);
+        for (int u = 0; u < 2; ++u) {
+          const int kt = kc * 2 + u;
+          const u32x4 kx = *reinterpret_cast<const u32x4 *>(&Ks[(kt * 32 + n) * LDK + c * 16 + hi * 8]);
+          sacc[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kx), qf[c],
+                                                            sacc[u], 0, 0, 0);
+        }
       }
-    }
-
-    // ---- masks: token causality inside the diagonal block, ragged tail
-    if (j == r.i || nvalid < B) {
+      // masks: token causality inside the diagonal block, ragged tail
+      if (j == r.i || nvalid < B) {
 #pragma unroll
-      for (int kt = 0; kt < KT; ++kt)
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+          for (int q = 0; q < 16; ++q) {
+            const int kk = (kc * 2 + u) * 32 + 8 * (q >> 2) + 4 * hi + (q & 3);
+            if (key0 + kk > qloc || kk >= nvalid) sacc[u][q] = -INFINITY;
+          }
+      }
+      // online softmax (row statistics shared by lanes l and l^32).  The
+      // reference maximum only moves when some row's chunk maximum exceeds
+      // it by more than 2^8 in the exp2 domain: probabilities then stay
+      // <= 256 and the rescale of the output accumulators is skipped for
+      // most chunks.
+      float bm = -INFINITY;
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int q = 0; q < 16; ++q) bm = fmaxf(bm, sacc[u][q]);
+      bm = fmaxf(bm, __shfl_xor(bm, 32));
+      if (__ballot((bm - mrun) * cl2 > kRescaleLog2) != 0) {
+        const float mnew = fmaxf(mrun, bm);   // finite: every row sees at least one key
+        const float alpha = __builtin_amdgcn_exp2f((mrun - mnew) * cl2);
+        lrun *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) oacc[dt] *= alpha;
+        mrun = mnew;
+      }
+      const float msc = mrun * cl2;
+      float ps = 0.f;
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
 #pragma unroll
         for (int q = 0; q < 16; ++q) {
-          const int kk = kt * 32 + 8 * (q >> 2) + 4 * hi + (q & 3);
-          if (key0 + kk > qloc || kk >= nvalid) sacc[kt][q] = -INFINITY;
+          const float p = __builtin_amdgcn_exp2f(fmaf(sacc[u][q], cl2, -msc));
+          sacc[u][q] = p;
+          ps += p;
         }
-    }
-
-    // ---- online softmax (row statistics shared by lanes l and l^32)
-    float bm = -INFINITY;
+      lrun += ps;
+      // O^T += V^T P^T; contraction step (kt, hc) covers keys
+      //   kt*32 + 16hc + {4hi..4hi+3} and kt*32 + 16hc + 8 + {4hi..4hi+3}
 #pragma unroll
-    for (int kt = 0; kt < KT; ++kt)
+      for (int u = 0; u < 2; ++u) {
+        const int kt = kc * 2 + u;
 #pragma unroll
-      for (int q = 0; q < 16; ++q) bm = fmaxf(bm, sacc[kt][q]);
-    bm = fmaxf(bm, __shfl_xor(bm, 32));
-    const float mnew = fmaxf(mrun, bm);   // finite: every row sees at least one key
-    const float alpha = __builtin_amdgcn_exp2f((mrun - mnew) * cl2);
-    const float msc = mnew * cl2;
-    float ps = 0.f;
+        for (int hc = 0; hc < 2; ++hc) {
+          const f32x8 pv = {sacc[u][8 * hc + 0], sacc[u][8 * hc + 1], sacc[u][8 * hc + 2],
+                            sacc[u][8 * hc + 3], sacc[u][8 * hc + 4], sacc[u][8 * hc + 5],
+                            sacc[u][8 * hc + 6], sacc[u][8 * hc + 7]};
+          const bf16x8 pf = __builtin_convertvector(pv, bf16x8);
+          const int kb = kt * 32 + 16 * hc + 4 * hi;
 #pragma unroll
-    for (int kt = 0; kt < KT; ++kt)
-#pragma unroll
-      for (int q = 0; q < 16; ++q) {
-        const float p = __builtin_amdgcn_exp2f(fmaf(sacc[kt][q], cl2, -msc));
-        sacc[kt][q] = p;
-        ps += p;
-      }
-    lrun = fmaf(lrun, alpha, ps);
-    mrun = mnew;
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) oacc[dt] *= alpha;
-
-    // ---- O^T += V^T P^T; contraction chunk (kt, hc) covers keys
-    //      kt*32 + 16hc + {4hi..4hi+3} and kt*32 + 16hc + 8 + {4hi..4hi+3}
-#pragma unroll
-    for (int kt = 0; kt < KT; ++kt) {
-#pragma unroll
-      for (int hc = 0; hc < 2; ++hc) {
-        u32x4 pp;
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          pp[e] = pack_bf16x2(sacc[kt][8 * hc + 2 * e], sacc[kt][8 * hc + 2 * e + 1]);
-        const bf16x8 pf = __builtin_bit_cast(bf16x8, pp);
-        const int kb = kt * 32 + 16 * hc + 4 * hi;
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-          const uint16_t *vp = &Vt[(dt * 32 + n) * LDV + kb];
-          u32x4 vx;
-          vx[0] = *reinterpret_cast<const uint32_t *>(vp);
-          vx[1] = *reinterpret_cast<const uint32_t *>(vp + 2);
-          vx[2] = *reinterpret_cast<const uint32_t *>(vp + 8);
-          vx[3] = *reinterpret_cast<const uint32_t *>(vp + 10);
-          oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vx), pf,
-                                                             oacc[dt], 0, 0, 0);
+          for (int dt = 0; dt < DT; ++dt) {
+            const uint16_t *vp = &Vt[(dt * 32 + n) * LDV + kb];
+            u32x4 vx;
+            vx[0] = *reinterpret_cast<const uint32_t *>(vp);
+            vx[1] = *reinterpret_cast<const uint32_t *>(vp + 2);
+            vx[2] = *reinterpret_cast<const uint32_t *>(vp + 8);
+            vx[3] = *reinterpret_cast<const uint32_t *>(vp + 10);
+            oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vx), pf,
+                                                               oacc[dt], 0, 0, 0);
+          }
         }
       }
     }
