@@ -26,6 +26,8 @@
 // work, query head within the group): the query heads sharing a KV head and
 // the neighbouring rows (which keep mostly the same key blocks) then hit
 // the same L2.
+#include <type_traits>
+
 #include "stem_device.h"
 
 namespace stem {
@@ -77,33 +79,94 @@ __device__ __forceinline__ bool decode_item(const AttnArgs &a, Row &r) {
 
 // ---------------------------------------------------------------------------
 // bf16 inputs
+//
+// Workgroup = B/16 wavefronts for one (head, query block) row: B/32 query
+// groups of 32 tokens x 2 key halves.  Wavefront (qg, kh) owns queries
+// qg*32 .. qg*32+31 and, of every key block, keys kh*B/2 .. kh*B/2 + B/2-1;
+// the two key halves keep separate softmax statistics and are merged through
+// LDS at the end.  At about 180 registers per lane, two wavefronts share each
+// SIMD: one's softmax runs on the vector ALU while the other's MFMAs run.
+//
+// K and V tiles are double-buffered in LDS and filled by direct
+// global->LDS DMA (global_load_lds_dwordx4, no registers), one block ahead
+// of the compute.  Both tiles are row-major with an XOR swizzle of the
+// 16-byte chunks: K operand reads (ds_read_b128 of one key row) and V
+// operand reads (ds_read_b64_tr_b16, which hands each lane 4 consecutive
+// keys of one head-dim column, i.e. V^T) are free of bank conflicts.
+//
+// Selection lists are ascending and end with the diagonal block (the only
+// block that needs the token-level causal mask, and the only one that can
+// be a partial block): the loop runs the unmasked step over all entries but
+// the last, and the masked step once after it.
 
-// Two wavefronts per SIMD: while one runs softmax on the vector ALU the other
-// keeps the matrix cores busy, and one workgroup's global loads overlap the
-// other's compute.  That caps a wavefront at 256 registers.
+__device__ __forceinline__ int swz_k(int row, int nch) { return (row / (16 / nch)) % nch; }
+__device__ __forceinline__ int swz_v(int row, int nch) {
+  return nch == 16 ? 4 * (row % 4) : 4 * ((row / 2) % 2);
+}
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef short v8i16 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+typedef __attribute__((address_space(3))) void lds_void;
+
+// One wavefront-wide 16-byte-per-lane DMA from global memory into LDS:
+// lane l's 16 bytes land at LDS byte address lds_addr + 16 l.  Issued from
+// inline assembly so that the compiler does not track the LDS write: it
+// would otherwise wait for the in-flight prefetch of the next tile before
+// every read of the current one.  The kernel orders the DMA explicitly
+// (s_waitcnt vmcnt(0) + barrier before a tile is read).  The global address
+// is a wave-uniform base (SGPRs) plus a 32-bit per-lane byte offset; M0,
+// which carries the LDS address, is saved and restored around the DMA.
+__device__ __forceinline__ void dma16(const void *gbase, uint32_t voff, uint32_t lds_addr) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %2\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(voff), "s"(gbase), "s"(lds_addr)
+      : "memory");
+}
+
+// s_waitcnt vmcnt(0) (expcnt and lgkmcnt untouched), as a builtin so that the
+// compiler's own wait-count bookkeeping sees it.
+__device__ __forceinline__ void wait_vm() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 template <int B, int D, bool OUT_BF16>
-__global__ __launch_bounds__(B * 2) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__(B * 4) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_bf16_kernel(AttnArgs a) {
-  constexpr int NW = B / 32;           // wavefronts
+  constexpr int NQG = B / 32;          // query groups of 32
+  constexpr int NW = NQG * 2;          // wavefronts
   constexpr int NT = NW * 64;          // threads
-  constexpr int LDK = D + 8;           // K row stride in LDS (bf16 elements)
-  constexpr int LDV = B + 2;           // V^T row stride in LDS (bf16 elements)
+  constexpr int KH = B / 2;            // keys per wavefront per block
+  constexpr int KT = KH / 32;          // 32-key MFMA tiles per wavefront per block
   constexpr int DT = D / 32;           // 32-dim output tiles
   constexpr int DC = D / 16;           // 16-dim contraction chunks for S
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[B * LDK];
-  __shared__ __attribute__((aligned(16))) uint16_t Vt[D * LDV];
+  constexpr int NCH = D / 8;           // 16-byte chunks per row
+  constexpr int ROWB = D * 2;          // bytes per K/V row
+  constexpr int TILEB = B * ROWB;      // bytes per K or V tile
+  constexpr int LOADS = TILEB / 16 / NT;
+  static_assert(LOADS * 16 * NT == TILEB, "tile must split into 16-byte loads");
+  static_assert(NT % NCH == 0, "a load step covers whole rows");
+  // [K buf 0][K buf 1][V buf 0][V buf 1]
+  __shared__ __attribute__((aligned(16))) char lds[4 * TILEB];
 
   Row r;
   if (!decode_item(a, r)) return;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int w = tid >> 6;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 31;
   const int hi = lane >> 5;
+  const int qg = w % NQG;
+  const int kh = w / NQG;
   const int Hq = a.Hq, Hkv = a.Hkv;
+  const uint32_t lds_base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void *)lds));
 
-  // this lane's query token (local position) and its Q fragment
-  const int qloc = r.i * B + w * 32 + n;
+  // Q fragment of this wavefront's 32 queries (B operand of S^T = K Q^T)
+  const int qloc = r.i * B + qg * 32 + n;
   const bool qvalid = qloc < r.seq_len;
   bf16x8 qf[DC];
   {
@@ -115,6 +178,7 @@ void attn_bf16_kernel(AttnArgs a) {
       qf[c] = __builtin_bit_cast(bf16x8, x);
     }
   }
+  wait_vm();  // Q resident before the loop: no wait on it inside
 
   f32x16 oacc[DT];
 #pragma unroll
@@ -122,154 +186,204 @@ void attn_bf16_kernel(AttnArgs a) {
   float mrun = -INFINITY, lrun = 0.f;
   const float cl2 = a.scale_log2;
 
+  // Stage key block j into buffer `buf` (asynchronous).  Thread tid moves
+  // 16-byte chunk slot q = it*NT + tid of each tile: row q / NCH, physical
+  // chunk q % NCH, which holds logical chunk (q % NCH) ^ swizzle(row).  The
+  // byte offsets of these chunks inside a block do not depend on the block
+  // and are computed once.  A final partial block reads its last valid row
+  // in place of the missing ones (those keys are masked).
+  constexpr int ROWSTEP = NT / NCH;
+  const int row0 = tid / NCH;
+  const int pc0 = tid % NCH;
+  const uint32_t rowbytes = static_cast<uint32_t>(Hkv) * D * 2;   // between token rows
+  uint32_t koff[LOADS], voff[LOADS];
+#pragma unroll
+  for (int it = 0; it < LOADS; ++it) {
+    const int row = row0 + it * ROWSTEP;
+    koff[it] = row * rowbytes + (pc0 ^ swz_k(row, NCH)) * 16;
+    voff[it] = row * rowbytes + (pc0 ^ swz_v(row, NCH)) * 16;
+  }
   const uint16_t *kbase = static_cast<const uint16_t *>(a.k);
   const uint16_t *vbase = static_cast<const uint16_t *>(a.v);
-
-  for (int t = 0; t < r.nkeep; ++t) {
-    const int j = __builtin_amdgcn_readfirstlane(r.list[t]);
-    if (j < 0 || j > r.i) continue;                       // not a causal block of this row
-    const int key0 = j * B;                               // local position of first key
-    const int nvalid = min(B, r.seq_len - key0);
-    const int64_t tok0 = r.seq_start + key0;
-
-    // ---- stage K (row-major) and V (transposed) into LDS
-    if (t > 0) __syncthreads();
+  auto issue = [&](int j, int buf) {
+    const int nvalid = min(B, r.seq_len - j * B);
+    const int64_t e0 = ((r.seq_start + int64_t(j) * B) * Hkv + r.g) * int64_t(D);
+    const uint16_t *kblk = kbase + e0;
+    const uint16_t *vblk = vbase + e0;
+    const uint32_t l0 = lds_base + w * 64 * 16;  // this wavefront's 1 KiB slab
+    if (nvalid == B) {
 #pragma unroll
-    for (int it = 0; it < (B * D / 8) / NT; ++it) {
-      const int c = tid + it * NT;
-      const int key = c / (D / 8);
-      const int dc = c % (D / 8);
-      u32x4 x = u32x4{0u, 0u, 0u, 0u};
-      if (key < nvalid)
-        x = *reinterpret_cast<const u32x4 *>(kbase + ((tok0 + key) * Hkv + r.g) * int64_t(D) + dc * 8);
-      *reinterpret_cast<u32x4 *>(&Ks[key * LDK + dc * 8]) = x;
-    }
+      for (int it = 0; it < LOADS; ++it) {
+        dma16(kblk, koff[it], l0 + it * NT * 16 + buf * TILEB);
+        dma16(vblk, voff[it], l0 + it * NT * 16 + (2 + buf) * TILEB);
+      }
+    } else {
 #pragma unroll
-    for (int it = 0; it < (B / 2 * D / 8) / NT; ++it) {
-      const int c = tid + it * NT;
-      const int kp = c / (D / 8);
-      const int dc = c % (D / 8);
-      u32x4 x0 = u32x4{0u, 0u, 0u, 0u}, x1 = u32x4{0u, 0u, 0u, 0u};
-      if (2 * kp < nvalid)
-        x0 = *reinterpret_cast<const u32x4 *>(vbase + ((tok0 + 2 * kp) * Hkv + r.g) * int64_t(D) + dc * 8);
-      if (2 * kp + 1 < nvalid)
-        x1 = *reinterpret_cast<const u32x4 *>(vbase + ((tok0 + 2 * kp + 1) * Hkv + r.g) * int64_t(D) + dc * 8);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint32_t lo = __builtin_amdgcn_perm(x1[e], x0[e], 0x05040100u);  // (x0.lo, x1.lo)
-        const uint32_t hi2 = __builtin_amdgcn_perm(x1[e], x0[e], 0x07060302u); // (x0.hi, x1.hi)
-        *reinterpret_cast<uint32_t *>(&Vt[(dc * 8 + 2 * e) * LDV + 2 * kp]) = lo;
-        *reinterpret_cast<uint32_t *>(&Vt[(dc * 8 + 2 * e + 1) * LDV + 2 * kp]) = hi2;
+      for (int it = 0; it < LOADS; ++it) {
+        const int row = row0 + it * ROWSTEP;
+        const uint32_t rb = min(row, nvalid - 1) * rowbytes;
+        dma16(kblk, rb + (pc0 ^ swz_k(row, NCH)) * 16, l0 + it * NT * 16 + buf * TILEB);
+        dma16(vblk, rb + (pc0 ^ swz_v(row, NCH)) * 16, l0 + it * NT * 16 + (2 + buf) * TILEB);
       }
     }
-    __syncthreads();
+  };
 
-    // ---- the key block in chunks of 64 keys (two 32-key sub-tiles)
+  // lane constants of the V^T operand reads (see the PV step)
+  const int vrow = 4 * hi + ((lane & 15) >> 2);
+  const int vd = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  const int vsub = ((vd & 7) >> 2) * 8;
+
+  // One key block held in buffer `buf`: S, (mask), softmax, PV.
+  auto step = [&](auto mask_tag, int buf, int key0, int nvalid) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+    const char *Kb = lds + buf * TILEB;
+    const char *Vb = lds + (2 + buf) * TILEB;
 #pragma unroll
-    for (int kc = 0; kc < B / 64; ++kc) {
-      // S^T = K Q^T for this chunk
-      f32x16 sacc[2];
-      sacc[0] = f32x16{};
-      sacc[1] = f32x16{};
+    for (int u = 0; u < KT; ++u) {
+      // S^T = K Q^T for keys kh*KH + 32u .. +31
+      f32x16 sacc = f32x16{};
+      const int kr = kh * KH + u * 32 + n;
+      const char *krow = Kb + kr * ROWB;
+      const int ksw = swz_k(kr, NCH);
 #pragma unroll
       for (int c = 0; c < DC; ++c) {
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const int kt = kc * 2 + u;
-          const u32x4 kx = *reinterpret_cast<const u32x4 *>(&Ks[(kt * 32 + n) * LDK + c * 16 + hi * 8]);
-          sacc[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kx), qf[c],
-                                                            sacc[u], 0, 0, 0);
-        }
+        const u32x4 kx = *reinterpret_cast<const u32x4 *>(krow + (((2 * c + hi) ^ ksw) * 16));
+        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kx), qf[c], sacc,
+                                                      0, 0, 0);
       }
-      // masks: token causality inside the diagonal block, ragged tail
-      if (j == r.i || nvalid < B) {
+      if constexpr (MASK) {
+        // key position <= query position, and inside the valid rows
+        const int lim = min(qloc - key0, nvalid - 1) - (kh * KH + u * 32 + 4 * hi);
 #pragma unroll
-        for (int u = 0; u < 2; ++u)
-#pragma unroll
-          for (int q = 0; q < 16; ++q) {
-            const int kk = (kc * 2 + u) * 32 + 8 * (q >> 2) + 4 * hi + (q & 3);
-            if (key0 + kk > qloc || kk >= nvalid) sacc[u][q] = -INFINITY;
-          }
+        for (int q = 0; q < 16; ++q)
+          if (8 * (q >> 2) + (q & 3) > lim) sacc[q] = -INFINITY;
       }
-      // online softmax (row statistics shared by lanes l and l^32).  The
-      // reference maximum only moves when some row's chunk maximum exceeds
-      // it by more than 2^8 in the exp2 domain: probabilities then stay
-      // <= 256 and the rescale of the output accumulators is skipped for
-      // most chunks.
+      // online softmax; the reference maximum moves only when a row's
+      // maximum exceeds it by more than 2^8 in the exp2 domain, so most
+      // steps skip rescaling the accumulators
       float bm = -INFINITY;
 #pragma unroll
-      for (int u = 0; u < 2; ++u)
-#pragma unroll
-        for (int q = 0; q < 16; ++q) bm = fmaxf(bm, sacc[u][q]);
+      for (int q = 0; q < 16; ++q) bm = fmaxf(bm, sacc[q]);
       bm = fmaxf(bm, __shfl_xor(bm, 32));
-      if (__ballot((bm - mrun) * cl2 > kRescaleLog2) != 0) {
-        const float mnew = fmaxf(mrun, bm);   // finite: every row sees at least one key
-        const float alpha = __builtin_amdgcn_exp2f((mrun - mnew) * cl2);
+      if (__ballot((bm - mrun) * cl2 > kRescaleLog2)) {
+        const float mnew = fmaxf(mrun, bm);
+        const float alpha = mnew == mrun ? 1.f : __builtin_amdgcn_exp2f((mrun - mnew) * cl2);
         lrun *= alpha;
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) oacc[dt] *= alpha;
         mrun = mnew;
       }
-      const float msc = mrun * cl2;
+      // rows with every key so far masked keep mrun = -inf and p = 0
+      const float msc = mrun == -INFINITY ? 0.f : mrun * cl2;
       float ps = 0.f;
 #pragma unroll
-      for (int u = 0; u < 2; ++u)
-#pragma unroll
-        for (int q = 0; q < 16; ++q) {
-          const float p = __builtin_amdgcn_exp2f(fmaf(sacc[u][q], cl2, -msc));
-          sacc[u][q] = p;
-          ps += p;
-        }
+      for (int q = 0; q < 16; ++q) {
+        const float p = __builtin_amdgcn_exp2f(fmaf(sacc[q], cl2, -msc));
+        sacc[q] = p;
+        ps += p;
+      }
       lrun += ps;
-      // O^T += V^T P^T; contraction step (kt, hc) covers keys
-      //   kt*32 + 16hc + {4hi..4hi+3} and kt*32 + 16hc + 8 + {4hi..4hi+3}
+      // O^T += V^T P^T.  Contraction step hc covers keys kb0 + 4hi + {0..3}
+      // and kb0 + 8 + 4hi + {0..3} with kb0 = kh*KH + 32u + 16hc;
+      // ds_read_b64_tr_b16 gives lane (n, hi) V[kb0 + 4hi + e][dt*32 + n].
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int kt = kc * 2 + u;
+      for (int hc = 0; hc < 2; ++hc) {
+        const f32x8 pv = {sacc[8 * hc + 0], sacc[8 * hc + 1], sacc[8 * hc + 2], sacc[8 * hc + 3],
+                          sacc[8 * hc + 4], sacc[8 * hc + 5], sacc[8 * hc + 6], sacc[8 * hc + 7]};
+        const bf16x8 pf = __builtin_convertvector(pv, bf16x8);
+        const int r0 = kh * KH + u * 32 + 16 * hc + vrow;
+        const char *p0 = Vb + r0 * ROWB + vsub;
+        const char *p1 = p0 + 8 * ROWB;
+        const int sw0 = swz_v(r0, NCH), sw1 = swz_v(r0 + 8, NCH);
 #pragma unroll
-        for (int hc = 0; hc < 2; ++hc) {
-          const f32x8 pv = {sacc[u][8 * hc + 0], sacc[u][8 * hc + 1], sacc[u][8 * hc + 2],
-                            sacc[u][8 * hc + 3], sacc[u][8 * hc + 4], sacc[u][8 * hc + 5],
-                            sacc[u][8 * hc + 6], sacc[u][8 * hc + 7]};
-          const bf16x8 pf = __builtin_convertvector(pv, bf16x8);
-          const int kb = kt * 32 + 16 * hc + 4 * hi;
-#pragma unroll
-          for (int dt = 0; dt < DT; ++dt) {
-            const uint16_t *vp = &Vt[(dt * 32 + n) * LDV + kb];
-            u32x4 vx;
-            vx[0] = *reinterpret_cast<const uint32_t *>(vp);
-            vx[1] = *reinterpret_cast<const uint32_t *>(vp + 2);
-            vx[2] = *reinterpret_cast<const uint32_t *>(vp + 8);
-            vx[3] = *reinterpret_cast<const uint32_t *>(vp + 10);
-            oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vx), pf,
-                                                               oacc[dt], 0, 0, 0);
-          }
+        for (int dt = 0; dt < DT; ++dt) {
+          const int ch = (dt * 32 + vd) >> 3;
+          const v4i16 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(p0 + ((ch ^ sw0) * 16)));
+          const v4i16 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(p1 + ((ch ^ sw1) * 16)));
+          const bf16x8 vf = __builtin_bit_cast(bf16x8, (v8i16){v0[0], v0[1], v0[2], v0[3],
+                                                               v1[0], v1[1], v1[2], v1[3]});
+          oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf, oacc[dt], 0, 0, 0);
         }
       }
     }
+  };
+
+  // Kept block numbers, 64 at a time in one register (lane e holds entry
+  // chunk + e); entries outside [0, i] are clamped so that no access leaves
+  // the sequence.
+  const int nkeep = r.nkeep;
+  int chunk = 0;
+  int listv = lane < nkeep ? min(max(r.list[lane], 0), r.i) : 0;
+  auto entry = [&](int t) {
+    if (t >= chunk + 64) {
+      chunk += 64;
+      listv = chunk + lane < nkeep ? min(max(r.list[chunk + lane], 0), r.i) : 0;
+    }
+    return __builtin_amdgcn_readlane(listv, t - chunk);
+  };
+
+  if (nkeep > 0) {
+    int jnext = entry(0);
+    issue(jnext, 0);
+    for (int t = 0; t + 1 < nkeep; ++t) {
+      const int j = jnext;
+      // tile t is resident once this wavefront's DMA has landed and every
+      // wavefront has passed the barrier (which also frees the other buffer)
+      wait_vm();
+      __syncthreads();
+      jnext = entry(t + 1);
+      issue(jnext, (t + 1) & 1);
+      step(std::false_type{}, t & 1, j * B, B);
+    }
+    wait_vm();
+    __syncthreads();
+    step(std::true_type{}, (nkeep - 1) & 1, jnext * B, min(B, r.seq_len - jnext * B));
   }
 
-  // ---- finalize: O^T lane layout = query n, dims dt*32 + 8(q/4) + 4hi + q%4
-  const float ltot = lrun + __shfl_xor(lrun, 32);
+  // ---- merge the two key halves through LDS (buffers are free now)
+  __syncthreads();
+  float *mo = reinterpret_cast<float *>(lds);   // [NQG][DT][16][64] partial O
+  float *ml = mo + NQG * DT * 16 * 64;          // [NQG][2][64]: m, l
+  if (kh == 1) {
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) mo[((qg * DT + dt) * 16 + e) * 64 + lane] = oacc[dt][e];
+    ml[(qg * 2 + 0) * 64 + lane] = mrun;
+    ml[(qg * 2 + 1) * 64 + lane] = lrun;
+  }
+  __syncthreads();
+  if (kh == 1) return;
+  const float m1 = ml[(qg * 2 + 0) * 64 + lane];
+  const float l1 = ml[(qg * 2 + 1) * 64 + lane];
+  const float M = fmaxf(mrun, m1);          // finite: key 0 of the diagonal is in half 0
+  const float f0 = mrun == M ? 1.f : __builtin_amdgcn_exp2f((mrun - M) * cl2);
+  const float f1 = m1 == -INFINITY ? 0.f : (m1 == M ? 1.f : __builtin_amdgcn_exp2f((m1 - M) * cl2));
+  const float lsum = lrun * f0 + l1 * f1;
+  const float ltot = lsum + __shfl_xor(lsum, 32);
   if (!qvalid) return;
   const float inv = 1.0f / ltot;
   const int64_t orow = ((r.seq_start + qloc) * Hq + r.h) * int64_t(D);
 #pragma unroll
-  for (int dt = 0; dt < DT; ++dt)
+  for (int dt = 0; dt < DT; ++dt) {
+    f32x16 o;
+#pragma unroll
+    for (int e = 0; e < 16; ++e)
+      o[e] = (oacc[dt][e] * f0 + mo[((qg * DT + dt) * 16 + e) * 64 + lane] * f1) * inv;
 #pragma unroll
     for (int rg = 0; rg < 4; ++rg) {
       const int d0 = dt * 32 + 8 * rg + 4 * hi;
-      const float o0 = oacc[dt][4 * rg] * inv, o1 = oacc[dt][4 * rg + 1] * inv;
-      const float o2 = oacc[dt][4 * rg + 2] * inv, o3 = oacc[dt][4 * rg + 3] * inv;
       if (OUT_BF16) {
         uint32_t *op = reinterpret_cast<uint32_t *>(static_cast<uint16_t *>(a.out) + orow + d0);
-        op[0] = pack_bf16x2(o0, o1);
-        op[1] = pack_bf16x2(o2, o3);
+        op[0] = pack_bf16x2(o[4 * rg], o[4 * rg + 1]);
+        op[1] = pack_bf16x2(o[4 * rg + 2], o[4 * rg + 3]);
       } else {
-        *reinterpret_cast<f32x4 *>(static_cast<float *>(a.out) + orow + d0) = f32x4{o0, o1, o2, o3};
+        *reinterpret_cast<f32x4 *>(static_cast<float *>(a.out) + orow + d0) =
+            f32x4{o[4 * rg], o[4 * rg + 1], o[4 * rg + 2], o[4 * rg + 3]};
       }
     }
-  if (a.lse && hi == 0) a.lse[int64_t(r.h) * a.T + r.seq_start + qloc] = mrun * a.scale + logf(ltot);
+  }
+  if (a.lse && hi == 0) a.lse[int64_t(r.h) * a.T + r.seq_start + qloc] = M * a.scale + logf(ltot);
 }
 
 // ---------------------------------------------------------------------------
@@ -419,7 +533,7 @@ struct Dummy;
 template <bool BF16IN, int B, int D, bool OB>
 hipError_t launch_one(const AttnArgs &a, dim3 grid, hipStream_t st) {
   if (BF16IN)
-    hipLaunchKernelGGL((attn_bf16_kernel<B, D, OB>), grid, dim3(B * 2), 0, st, a);
+    hipLaunchKernelGGL((attn_bf16_kernel<B, D, OB>), grid, dim3(B * 4), 0, st, a);
   else
     hipLaunchKernelGGL((attn_f32_kernel<B, D, OB>), grid, dim3(B * 2), 0, st, a);
   return hipGetLastError();
