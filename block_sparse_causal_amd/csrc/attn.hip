@@ -80,24 +80,24 @@ __device__ __forceinline__ bool decode_item(const AttnArgs &a, Row &r) {
 // ---------------------------------------------------------------------------
 // bf16 inputs
 //
-// Workgroup = B/16 wavefronts for one (head, query block) row: B/32 query
-// groups of 32 tokens x 2 key halves.  Wavefront (qg, kh) owns queries
-// qg*32 .. qg*32+31 and, of every key block, keys kh*B/2 .. kh*B/2 + B/2-1;
-// the two key halves keep separate softmax statistics and are merged through
-// LDS at the end.  At about 180 registers per lane, two wavefronts share each
-// SIMD: one's softmax runs on the vector ALU while the other's MFMAs run.
+// Workgroup = B/32 wavefronts for one (head, query block) row, wavefront w
+// owning queries 32w .. 32w+31.  Each kept key block is streamed through
+// LDS in two stages of B/2 keys; stages are double-buffered and filled by
+// direct global->LDS DMA (global_load_lds_dwordx4, no registers) one stage
+// ahead of the compute.  A workgroup then needs 4 B/2 d 2 bytes of LDS
+// (64 KiB at B = d = 128), so two workgroups share a CU: their barriers are
+// independent, and one's softmax, LDS reads and DMA waits overlap the
+// other's MFMAs on the same SIMDs.
 //
-// K and V tiles are double-buffered in LDS and filled by direct
-// global->LDS DMA (global_load_lds_dwordx4, no registers), one block ahead
-// of the compute.  Both tiles are row-major with an XOR swizzle of the
-// 16-byte chunks: K operand reads (ds_read_b128 of one key row) and V
-// operand reads (ds_read_b64_tr_b16, which hands each lane 4 consecutive
-// keys of one head-dim column, i.e. V^T) are free of bank conflicts.
+// K and V stages are row-major with an XOR swizzle of the 16-byte chunks:
+// K operand reads (ds_read_b128 of one key row) and V operand reads
+// (ds_read_b64_tr_b16, which hands each lane 4 consecutive keys of one
+// head-dim column, i.e. V^T) are free of bank conflicts.
 //
 // Selection lists are ascending and end with the diagonal block (the only
 // block that needs the token-level causal mask, and the only one that can
-// be a partial block): the loop runs the unmasked step over all entries but
-// the last, and the masked step once after it.
+// be a partial block): the unmasked step runs for every stage of the other
+// blocks, the masked step for the two stages of the last one.
 
 __device__ __forceinline__ int swz_k(int row, int nch) { return (row / (16 / nch)) % nch; }
 __device__ __forceinline__ int swz_v(int row, int nch) {
@@ -112,11 +112,11 @@ typedef __attribute__((address_space(3))) void lds_void;
 // One wavefront-wide 16-byte-per-lane DMA from global memory into LDS:
 // lane l's 16 bytes land at LDS byte address lds_addr + 16 l.  Issued from
 // inline assembly so that the compiler does not track the LDS write: it
-// would otherwise wait for the in-flight prefetch of the next tile before
+// would otherwise wait for the in-flight prefetch of the next stage before
 // every read of the current one.  The kernel orders the DMA explicitly
-// (s_waitcnt vmcnt(0) + barrier before a tile is read).  The global address
-// is a wave-uniform base (SGPRs) plus a 32-bit per-lane byte offset; M0,
-// which carries the LDS address, is saved and restored around the DMA.
+// (s_waitcnt vmcnt(0) + barrier before a stage is read).  The global
+// address is a wave-uniform base (SGPRs) plus a 32-bit per-lane byte
+// offset; M0, which carries the LDS address, is saved and restored.
 __device__ __forceinline__ void dma16(const void *gbase, uint32_t voff, uint32_t lds_addr) {
   uint32_t saved;
   asm volatile(
@@ -135,20 +135,19 @@ __device__ __forceinline__ void dma16(const void *gbase, uint32_t voff, uint32_t
 __device__ __forceinline__ void wait_vm() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 template <int B, int D, bool OUT_BF16>
-__global__ __launch_bounds__(B * 4) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__(B * 2) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_bf16_kernel(AttnArgs a) {
-  constexpr int NQG = B / 32;          // query groups of 32
-  constexpr int NW = NQG * 2;          // wavefronts
+  constexpr int NW = B / 32;           // wavefronts, 32 queries each
   constexpr int NT = NW * 64;          // threads
-  constexpr int KH = B / 2;            // keys per wavefront per block
-  constexpr int KT = KH / 32;          // 32-key MFMA tiles per wavefront per block
+  constexpr int SK = B / 2;            // keys per stage
+  constexpr int KT = SK / 32;          // 32-key MFMA tiles per stage
   constexpr int DT = D / 32;           // 32-dim output tiles
   constexpr int DC = D / 16;           // 16-dim contraction chunks for S
   constexpr int NCH = D / 8;           // 16-byte chunks per row
   constexpr int ROWB = D * 2;          // bytes per K/V row
-  constexpr int TILEB = B * ROWB;      // bytes per K or V tile
+  constexpr int TILEB = SK * ROWB;     // bytes per K or V stage
   constexpr int LOADS = TILEB / 16 / NT;
-  static_assert(LOADS * 16 * NT == TILEB, "tile must split into 16-byte loads");
+  static_assert(LOADS * 16 * NT == TILEB, "a stage must split into 16-byte loads");
   static_assert(NT % NCH == 0, "a load step covers whole rows");
   // [K buf 0][K buf 1][V buf 0][V buf 1]
   __shared__ __attribute__((aligned(16))) char lds[4 * TILEB];
@@ -160,13 +159,11 @@ void attn_bf16_kernel(AttnArgs a) {
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 31;
   const int hi = lane >> 5;
-  const int qg = w % NQG;
-  const int kh = w / NQG;
   const int Hq = a.Hq, Hkv = a.Hkv;
   const uint32_t lds_base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void *)lds));
 
   // Q fragment of this wavefront's 32 queries (B operand of S^T = K Q^T)
-  const int qloc = r.i * B + qg * 32 + n;
+  const int qloc = r.i * B + w * 32 + n;
   const bool qvalid = qloc < r.seq_len;
   bf16x8 qf[DC];
   {
@@ -186,12 +183,12 @@ void attn_bf16_kernel(AttnArgs a) {
   float mrun = -INFINITY, lrun = 0.f;
   const float cl2 = a.scale_log2;
 
-  // Stage key block j into buffer `buf` (asynchronous).  Thread tid moves
-  // 16-byte chunk slot q = it*NT + tid of each tile: row q / NCH, physical
-  // chunk q % NCH, which holds logical chunk (q % NCH) ^ swizzle(row).  The
-  // byte offsets of these chunks inside a block do not depend on the block
-  // and are computed once.  A final partial block reads its last valid row
-  // in place of the missing ones (those keys are masked).
+  // Stage keys [key0, key0 + SK) of block j into buffer `buf` (asynchronous).
+  // Thread tid moves 16-byte chunk slot q = it*NT + tid: row q / NCH,
+  // physical chunk q % NCH, which holds logical chunk (q % NCH) ^ swizzle.
+  // The byte offsets inside a stage do not depend on the block and are
+  // computed once.  Rows past the end of a final partial block read its last
+  // valid row instead (those keys are masked).
   constexpr int ROWSTEP = NT / NCH;
   const int row0 = tid / NCH;
   const int pc0 = tid % NCH;
@@ -205,27 +202,30 @@ void attn_bf16_kernel(AttnArgs a) {
   }
   const uint16_t *kbase = static_cast<const uint16_t *>(a.k);
   const uint16_t *vbase = static_cast<const uint16_t *>(a.v);
-  auto issue = [&](int j, int buf) {
-    const int nvalid = min(B, r.seq_len - j * B);
-    const int64_t e0 = ((r.seq_start + int64_t(j) * B) * Hkv + r.g) * int64_t(D);
+  auto issue = [&](int j, int half, int buf) {
+    const int first = j * B + half * SK;                 // first key (local position)
+    const int nrows = min(SK, r.seq_len - first);         // may be <= 0 past the end
+    const int64_t e0 = ((r.seq_start + first) * Hkv + r.g) * int64_t(D);
     const uint16_t *kblk = kbase + e0;
     const uint16_t *vblk = vbase + e0;
     const uint32_t l0 = lds_base + w * 64 * 16;  // this wavefront's 1 KiB slab
-    if (nvalid == B) {
+    if (nrows == SK) {
 #pragma unroll
       for (int it = 0; it < LOADS; ++it) {
         dma16(kblk, koff[it], l0 + it * NT * 16 + buf * TILEB);
         dma16(vblk, voff[it], l0 + it * NT * 16 + (2 + buf) * TILEB);
       }
-    } else {
+    } else if (nrows > 0) {
 #pragma unroll
       for (int it = 0; it < LOADS; ++it) {
         const int row = row0 + it * ROWSTEP;
-        const uint32_t rb = min(row, nvalid - 1) * rowbytes;
+        const uint32_t rb = min(row, nrows - 1) * rowbytes;
         dma16(kblk, rb + (pc0 ^ swz_k(row, NCH)) * 16, l0 + it * NT * 16 + buf * TILEB);
         dma16(vblk, rb + (pc0 ^ swz_v(row, NCH)) * 16, l0 + it * NT * 16 + (2 + buf) * TILEB);
       }
     }
+    // nrows <= 0: the stage lies past the end of the sequence; its keys are
+    // all masked and the buffer is not read
   };
 
   // lane constants of the V^T operand reads (see the PV step)
@@ -233,16 +233,22 @@ void attn_bf16_kernel(AttnArgs a) {
   const int vd = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
   const int vsub = ((vd & 7) >> 2) * 8;
 
-  // One key block held in buffer `buf`: S, (mask), softmax, PV.
-  auto step = [&](auto mask_tag, int buf, int key0, int nvalid) {
+  // One stage held in buffer `buf`, first key at local position key0: S
+  // for KT tiles of 32 keys, (mask), softmax, PV.
+  auto step = [&](auto mask_tag, int buf, int key0) {
     constexpr bool MASK = decltype(mask_tag)::value;
+    if constexpr (MASK) {
+      // nothing visible to this wavefront in this stage (future keys or
+      // past the end of the sequence): skip it (wave-uniform)
+      if (key0 > r.i * B + w * 32 + 31 || key0 >= r.seq_len) return;
+    }
     const char *Kb = lds + buf * TILEB;
     const char *Vb = lds + (2 + buf) * TILEB;
 #pragma unroll
     for (int u = 0; u < KT; ++u) {
-      // S^T = K Q^T for keys kh*KH + 32u .. +31
+      // S^T = K Q^T for keys key0 + 32u .. +31
       f32x16 sacc = f32x16{};
-      const int kr = kh * KH + u * 32 + n;
+      const int kr = u * 32 + n;
       const char *krow = Kb + kr * ROWB;
       const int ksw = swz_k(kr, NCH);
 #pragma unroll
@@ -252,15 +258,15 @@ void attn_bf16_kernel(AttnArgs a) {
                                                       0, 0, 0);
       }
       if constexpr (MASK) {
-        // key position <= query position, and inside the valid rows
-        const int lim = min(qloc - key0, nvalid - 1) - (kh * KH + u * 32 + 4 * hi);
+        // key position <= query position, and inside the sequence
+        const int lim = min(qloc, r.seq_len - 1) - (key0 + u * 32 + 4 * hi);
 #pragma unroll
         for (int q = 0; q < 16; ++q)
           if (8 * (q >> 2) + (q & 3) > lim) sacc[q] = -INFINITY;
       }
       // online softmax; the reference maximum moves only when a row's
       // maximum exceeds it by more than 2^8 in the exp2 domain, so most
-      // steps skip rescaling the accumulators
+      // tiles skip rescaling the accumulators
       float bm = -INFINITY;
 #pragma unroll
       for (int q = 0; q < 16; ++q) bm = fmaxf(bm, sacc[q]);
@@ -284,14 +290,14 @@ void attn_bf16_kernel(AttnArgs a) {
       }
       lrun += ps;
       // O^T += V^T P^T.  Contraction step hc covers keys kb0 + 4hi + {0..3}
-      // and kb0 + 8 + 4hi + {0..3} with kb0 = kh*KH + 32u + 16hc;
+      // and kb0 + 8 + 4hi + {0..3} with kb0 = 32u + 16hc (stage rows);
       // ds_read_b64_tr_b16 gives lane (n, hi) V[kb0 + 4hi + e][dt*32 + n].
 #pragma unroll
       for (int hc = 0; hc < 2; ++hc) {
         const f32x8 pv = {sacc[8 * hc + 0], sacc[8 * hc + 1], sacc[8 * hc + 2], sacc[8 * hc + 3],
                           sacc[8 * hc + 4], sacc[8 * hc + 5], sacc[8 * hc + 6], sacc[8 * hc + 7]};
         const bf16x8 pf = __builtin_convertvector(pv, bf16x8);
-        const int r0 = kh * KH + u * 32 + 16 * hc + vrow;
+        const int r0 = u * 32 + 16 * hc + vrow;
         const char *p0 = Vb + r0 * ROWB + vsub;
         const char *p1 = p0 + 8 * ROWB;
         const int sw0 = swz_v(r0, NCH), sw1 = swz_v(r0 + 8, NCH);
@@ -322,68 +328,53 @@ void attn_bf16_kernel(AttnArgs a) {
     return __builtin_amdgcn_readlane(listv, t - chunk);
   };
 
+  // Stage s = 2t + half covers keys [half*SK, half*SK + SK) of entry t and
+  // lives in buffer s & 1.
   if (nkeep > 0) {
-    int jnext = entry(0);
-    issue(jnext, 0);
+    int jcur = entry(0);
+    issue(jcur, 0, 0);
     for (int t = 0; t + 1 < nkeep; ++t) {
-      const int j = jnext;
-      // tile t is resident once this wavefront's DMA has landed and every
-      // wavefront has passed the barrier (which also frees the other buffer)
       wait_vm();
       __syncthreads();
-      jnext = entry(t + 1);
-      issue(jnext, (t + 1) & 1);
-      step(std::false_type{}, t & 1, j * B, B);
+      issue(jcur, 1, 1);                      // second half of this block
+      step(std::false_type{}, 0, jcur * B);
+      const int jn = entry(t + 1);
+      wait_vm();
+      __syncthreads();
+      issue(jn, 0, 0);                        // first half of the next block
+      step(std::false_type{}, 1, jcur * B + SK);
+      jcur = jn;
     }
     wait_vm();
     __syncthreads();
-    step(std::true_type{}, (nkeep - 1) & 1, jnext * B, min(B, r.seq_len - jnext * B));
+    issue(jcur, 1, 1);
+    step(std::true_type{}, 0, jcur * B);
+    wait_vm();
+    __syncthreads();
+    step(std::true_type{}, 1, jcur * B + SK);
   }
 
-  // ---- merge the two key halves through LDS (buffers are free now)
-  __syncthreads();
-  float *mo = reinterpret_cast<float *>(lds);   // [NQG][DT][16][64] partial O
-  float *ml = mo + NQG * DT * 16 * 64;          // [NQG][2][64]: m, l
-  if (kh == 1) {
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) mo[((qg * DT + dt) * 16 + e) * 64 + lane] = oacc[dt][e];
-    ml[(qg * 2 + 0) * 64 + lane] = mrun;
-    ml[(qg * 2 + 1) * 64 + lane] = lrun;
-  }
-  __syncthreads();
-  if (kh == 1) return;
-  const float m1 = ml[(qg * 2 + 0) * 64 + lane];
-  const float l1 = ml[(qg * 2 + 1) * 64 + lane];
-  const float M = fmaxf(mrun, m1);          // finite: key 0 of the diagonal is in half 0
-  const float f0 = mrun == M ? 1.f : __builtin_amdgcn_exp2f((mrun - M) * cl2);
-  const float f1 = m1 == -INFINITY ? 0.f : (m1 == M ? 1.f : __builtin_amdgcn_exp2f((m1 - M) * cl2));
-  const float lsum = lrun * f0 + l1 * f1;
-  const float ltot = lsum + __shfl_xor(lsum, 32);
+  // ---- finalize: O^T lane layout = query n, dims dt*32 + 8(q/4) + 4hi + q%4
+  const float ltot = lrun + __shfl_xor(lrun, 32);
   if (!qvalid) return;
   const float inv = 1.0f / ltot;
   const int64_t orow = ((r.seq_start + qloc) * Hq + r.h) * int64_t(D);
 #pragma unroll
-  for (int dt = 0; dt < DT; ++dt) {
-    f32x16 o;
-#pragma unroll
-    for (int e = 0; e < 16; ++e)
-      o[e] = (oacc[dt][e] * f0 + mo[((qg * DT + dt) * 16 + e) * 64 + lane] * f1) * inv;
+  for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
     for (int rg = 0; rg < 4; ++rg) {
       const int d0 = dt * 32 + 8 * rg + 4 * hi;
+      const float o0 = oacc[dt][4 * rg] * inv, o1 = oacc[dt][4 * rg + 1] * inv;
+      const float o2 = oacc[dt][4 * rg + 2] * inv, o3 = oacc[dt][4 * rg + 3] * inv;
       if (OUT_BF16) {
         uint32_t *op = reinterpret_cast<uint32_t *>(static_cast<uint16_t *>(a.out) + orow + d0);
-        op[0] = pack_bf16x2(o[4 * rg], o[4 * rg + 1]);
-        op[1] = pack_bf16x2(o[4 * rg + 2], o[4 * rg + 3]);
+        op[0] = pack_bf16x2(o0, o1);
+        op[1] = pack_bf16x2(o2, o3);
       } else {
-        *reinterpret_cast<f32x4 *>(static_cast<float *>(a.out) + orow + d0) =
-            f32x4{o[4 * rg], o[4 * rg + 1], o[4 * rg + 2], o[4 * rg + 3]};
+        *reinterpret_cast<f32x4 *>(static_cast<float *>(a.out) + orow + d0) = f32x4{o0, o1, o2, o3};
       }
     }
-  }
-  if (a.lse && hi == 0) a.lse[int64_t(r.h) * a.T + r.seq_start + qloc] = M * a.scale + logf(ltot);
+  if (a.lse && hi == 0) a.lse[int64_t(r.h) * a.T + r.seq_start + qloc] = mrun * a.scale + logf(ltot);
 }
 
 // ---------------------------------------------------------------------------
@@ -533,7 +524,7 @@ struct Dummy;
 template <bool BF16IN, int B, int D, bool OB>
 hipError_t launch_one(const AttnArgs &a, dim3 grid, hipStream_t st) {
   if (BF16IN)
-    hipLaunchKernelGGL((attn_bf16_kernel<B, D, OB>), grid, dim3(B * 4), 0, st, a);
+    hipLaunchKernelGGL((attn_bf16_kernel<B, D, OB>), grid, dim3(B * 2), 0, st, a);
   else
     hipLaunchKernelGGL((attn_f32_kernel<B, D, OB>), grid, dim3(B * 2), 0, st, a);
   return hipGetLastError();
