@@ -20,7 +20,7 @@ namespace stem {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kUnroll = 4;
+constexpr int kUnroll = 8;
 
 struct PoolArgs {
   const void *q, *k, *v;

@@ -5,14 +5,15 @@
 // which orders key blocks of a row exactly like the pages' additive form
 // s_ij + beta * log ||V_j||^2 with beta = 1/2.
 //
-// One wavefront owns 32 consecutive query-block rows of one (query head,
-// sequence) and walks the causal key blocks 32 at a time.  The pooled dot
+// One workgroup owns 32 consecutive query-block rows of one (query head,
+// sequence); its 8 wavefronts split the causal key blocks 32 at a time
+// (round robin) and merge their row statistics through LDS.  The pooled dot
 // products are an f32 GEMM on the matrix cores (v_mfma_f32_32x32x2_f32,
 // computing the transposed tile keys x queries so that each lane holds one
 // query row's values and row statistics never leave the lane pair l, l^32).
-// Pass 1 stores the scaled logits into the output and keeps an online row
-// max / sum; pass 2 re-reads the lane's own values and rewrites them as
-// exp(x - max) / sum * vnorm.  f32 throughout.
+// Pass 1 keeps an online row max / sum (and the scaled logits, in registers
+// or parked in the output); pass 2 writes exp(x - max) / sum * vnorm.  f32
+// throughout; exponentials use the hardware exp2 (relative error ~1e-6).
 #include "stem_device.h"
 
 namespace stem {
@@ -27,10 +28,15 @@ struct ScoreArgs {
   float scale;
 };
 
+constexpr int kScoreWaves = 8;
+
 template <int D>
-__global__ __launch_bounds__(64) void score_kernel(ScoreArgs a) {
+__global__ __launch_bounds__(64 * kScoreWaves) void score_kernel(ScoreArgs a) {
   constexpr int HALF = D / 2;
-  const int lane = threadIdx.x;
+  __shared__ float st_m[kScoreWaves][64];
+  __shared__ float st_l[kScoreWaves][64];
+  const int lane = threadIdx.x & 63;
+  const int wv = threadIdx.x >> 6;
   const int n = lane & 31;        // query row inside the tile / key row of the A operand
   const int hi = lane >> 5;       // which half of the head dimension this lane feeds
   const int h = blockIdx.y;
@@ -66,59 +72,96 @@ __global__ __launch_bounds__(64) void score_kernel(ScoreArgs a) {
     }
   }
 
+  // pass 1: wavefront wv takes key tiles wv, wv + 8, ...; an online row
+  // max / sum is kept per lane.  The scaled logits of the first kKeep tiles
+  // stay in registers; those of later tiles are parked in the output and
+  // re-read in pass 2.
+  constexpr int kKeep = 4;
   float mrun = -INFINITY, lrun = 0.f;
   const int last_row = min(i0 + 31, nb - 1);
   const int jt_end = last_row / 32;
-  for (int jt = 0; jt <= jt_end; ++jt) {
-    const int j0 = jt * 32;
-    const int kr = j0 + n;
-    const bool kvalid = kr < nb;
+  f32x16 keep[kKeep];
+  auto load_k = [&](int jt, f32x4 (&kx)[HALF / 4]) {
+    const int kr = jt * 32 + n;
+    const bool kvalid = jt <= jt_end && kr < nb;
     const float *ksrc = a.kbar + (int64_t(g) * a.nbT + b0 + (kvalid ? kr : 0)) * D + hi * HALF;
+#pragma unroll
+    for (int c = 0; c < HALF / 4; ++c)
+      kx[c] = kvalid ? *reinterpret_cast<const f32x4 *>(ksrc + 4 * c) : f32x4{0.f, 0.f, 0.f, 0.f};
+  };
+  int slot = 0;
+  for (int jt = wv; jt <= jt_end; jt += kScoreWaves, ++slot) {
+    f32x4 kcur[HALF / 4];
+    load_k(jt, kcur);
     f32x16 acc = {};
 #pragma unroll
-    for (int c = 0; c < HALF; c += 4) {
-      f32x4 kx = kvalid ? *reinterpret_cast<const f32x4 *>(ksrc + c) : f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int c = 0; c < HALF / 4; ++c)
 #pragma unroll
       for (int e = 0; e < 4; ++e)
-        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(kx[e], qv[c + e], acc, 0, 0, 0);
-    }
+        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(kcur[c][e], qv[4 * c + e], acc, 0, 0, 0);
+    const int j0 = jt * 32;
     // acc[r] = logit(key j0 + 8(r/4) + 4hi + r%4, query qi)
     float bm = -INFINITY;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int j = j0 + 8 * (r >> 2) + 4 * hi + (r & 3);
-      const bool ok = qvalid && j <= qi;
-      const float x = acc[r] * a.scale;
-      acc[r] = ok ? x : -INFINITY;
-      if (ok) a.scores[rowbase + j] = x;
+      acc[r] = (qvalid && j <= qi) ? acc[r] * a.scale : -INFINITY;
       bm = fmaxf(bm, acc[r]);
     }
     const float mnew = fmaxf(mrun, bm);
     if (mnew != -INFINITY) {
       float ps = 0.f;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) ps += expf(acc[r] - mnew);
-      lrun = lrun * expf(mrun - mnew) + ps;
+      for (int r = 0; r < 16; ++r) ps += __expf(acc[r] - mnew);
+      lrun = lrun * __expf(mrun - mnew) + ps;
       mrun = mnew;
     }
+    if (slot < kKeep) {
+#pragma unroll
+      for (int k = 0; k < kKeep; ++k)
+        if (k == slot) keep[k] = acc;
+    } else {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int j = j0 + 8 * (r >> 2) + 4 * hi + (r & 3);
+        if (qvalid && j <= qi) a.scores[rowbase + j] = acc[r];
+      }
+    }
   }
-  // combine the two lanes that share a query row
-  const float mo = __shfl_xor(mrun, 32);
-  const float lo = __shfl_xor(lrun, 32);
-  const float M = fmaxf(mrun, mo);
-  const float L = (mrun == -INFINITY ? 0.f : lrun * expf(mrun - M)) +
-                  (mo == -INFINITY ? 0.f : lo * expf(mo - M));
+  // combine the statistics of the 8 wavefronts and of the two lanes that
+  // share a query row
+  st_m[wv][lane] = mrun;
+  st_l[wv][lane] = lrun;
+  __syncthreads();
+  float M = -INFINITY;
+#pragma unroll
+  for (int v = 0; v < kScoreWaves; ++v) M = fmaxf(M, fmaxf(st_m[v][lane], st_m[v][lane ^ 32]));
+  float L = 0.f;
+#pragma unroll
+  for (int v = 0; v < kScoreWaves; ++v) {
+    const float m0 = st_m[v][lane], m1 = st_m[v][lane ^ 32];
+    if (m0 != -INFINITY) L += st_l[v][lane] * __expf(m0 - M);
+    if (m1 != -INFINITY) L += st_l[v][lane ^ 32] * __expf(m1 - M);
+  }
   if (!qvalid) return;
+  // pass 2: write this wavefront's values as exp(x - M) / L * vnorm
   const float invL = 1.0f / L;
   const float *w = a.vnorm + int64_t(g) * a.nbT + b0;
-  for (int jt = 0; jt <= jt_end; ++jt) {
+  slot = 0;
+  for (int jt = wv; jt <= jt_end; jt += kScoreWaves, ++slot) {
     const int j0 = jt * 32;
+    f32x16 x;
+    if (slot < kKeep) {
+#pragma unroll
+      for (int k = 0; k < kKeep; ++k)
+        if (k == slot) x = keep[k];
+    }
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int j = j0 + 8 * (r >> 2) + 4 * hi + (r & 3);
       if (j <= qi) {
-        const float x = a.scores[rowbase + j];
-        a.scores[rowbase + j] = expf(x - M) * invL * w[j];
+        const float v = slot < kKeep ? x[r] : a.scores[rowbase + j];
+        a.scores[rowbase + j] = __expf(v - M) * invL * w[j];
       }
     }
   }
@@ -143,9 +186,9 @@ hipError_t launch_score(const stem_plan_info &in, PlanDev pd, const float *qbar,
   a.scale = 1.0f / sqrtf(static_cast<float>(in.head_dim));
   dim3 grid(static_cast<unsigned>(tiles), in.num_q_heads);
   if (in.head_dim == 128)
-    hipLaunchKernelGGL((score_kernel<128>), grid, dim3(64), 0, st, a);
+    hipLaunchKernelGGL((score_kernel<128>), grid, dim3(64 * kScoreWaves), 0, st, a);
   else
-    hipLaunchKernelGGL((score_kernel<64>), grid, dim3(64), 0, st, a);
+    hipLaunchKernelGGL((score_kernel<64>), grid, dim3(64 * kScoreWaves), 0, st, a);
   return hipGetLastError();
 }
 

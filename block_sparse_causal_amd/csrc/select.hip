@@ -5,10 +5,11 @@
 //
 // One 64-wide wavefront per (query head, query block) row.  The row's
 // candidate metrics are read once (coalesced) into registers as
-// order-preserving 32-bit keys.  The k-th largest key is found by a 32-step
-// bitwise bisection whose counts come from wavefront ballots (v_cmp straight
-// into a scalar mask, popcount on the scalar unit), so the cost does not
-// depend on k.  Keys above the threshold are kept; keys equal to it are kept
+// order-preserving 32-bit keys.  The k-th largest key is found by a bitwise
+// bisection (from the highest bit in which the row's largest and smallest
+// keys differ) whose counts come from wavefront ballots (v_cmp straight into
+// a scalar mask, popcount on the scalar unit), so the cost does not depend
+// on k.  Keys above the threshold are kept; keys equal to it are kept
 // in ascending block order until the budget is met, which is exactly "larger
 // metric first, equal metrics to the smaller block number".  The kept blocks
 // are written in ascending order with ballot/mbcnt compaction, after the
@@ -64,17 +65,38 @@ __global__ __launch_bounds__(256) void select_kernel(SelectArgs a) {
   }
   const float *mrow = a.scores + int64_t(h) * a.per_head + a.pd.tri[s] +
                       (int64_t(i) * (i + 1)) / 2;
-  uint32_t key[E];
+  // candidates j = S + lane + 64 e; every load is issued before any use
+  float mv[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) {
     const int j = S + lane + 64 * e;
-    key[e] = j < i ? order_key(mrow[j]) : 0u;
+    mv[e] = j < i ? mrow[j] : 0.f;
   }
+  uint32_t key[E];
+  uint32_t kmx = 0u, kmn = 0xffffffffu;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const bool c = S + lane + 64 * e < i;
+    key[e] = c ? order_key(mv[e]) : 0u;
+    kmx = c ? max(kmx, key[e]) : kmx;
+    kmn = c ? min(kmn, key[e]) : kmn;
+  }
+  const int ne = (ncand + 63) >> 6;  // chunks holding candidates (wave-uniform)
   // largest T with #{key >= T} >= take (take >= 1 here, and all
-  // candidates have key >= 1, so T >= 1 and padding never qualifies)
+  // candidates have key >= 1, so T >= 1 and padding never qualifies).
+  // T lies between the row's smallest and largest key, so the bits above
+  // their highest differing bit are already known.
   uint32_t T = 0;
   if (take > 0) {
-    for (int bit = 31; bit >= 0; --bit) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+      kmx = max(kmx, static_cast<uint32_t>(__shfl_xor(static_cast<int>(kmx), o)));
+      kmn = min(kmn, static_cast<uint32_t>(__shfl_xor(static_cast<int>(kmn), o)));
+    }
+    const uint32_t diff = kmx ^ kmn;
+    const int top = diff ? 31 - __builtin_clz(diff) : -1;
+    T = top < 0 ? kmx : (top >= 31 ? 0u : (kmx & ~((2u << top) - 1u)));
+    for (int bit = top; bit >= 0; --bit) {
       const uint32_t cand = T | (1u << bit);
       int cnt = 0;
 #pragma unroll
@@ -92,6 +114,7 @@ __global__ __launch_bounds__(256) void select_kernel(SelectArgs a) {
   int pos = S, eq_seen = 0;
 #pragma unroll
   for (int e = 0; e < E; ++e) {
+    if (e >= ne) break;
     const bool is_eq = take > 0 && key[e] == T;
     const uint64_t eqm = __ballot(is_eq);
     const int rank = eq_seen + static_cast<int>(lanes_below(eqm));
