@@ -21,6 +21,7 @@ Reported (one JSON line on stdout, progress on stderr):
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -50,6 +51,25 @@ def attn_flops(plan, diag_half: bool) -> float:
     if not diag_half:
         return full
     return full - 0.5 * per_tile * i.total_blocks * i.num_q_heads
+
+
+def traffic_record(workload: str):
+    """HBM bytes per attention launch measured by rocprofv3 (FETCH_SIZE and
+    WRITE_SIZE, copy-calibrated) and recorded under profiles/; returned only
+    if the attention kernel source is unchanged since that measurement."""
+    path = os.path.join(ROOT, "profiles", f"attn_{workload}.md")
+    src = os.path.join(ROOT, "block_sparse_causal_amd", "csrc", "attn.hip")
+    try:
+        rec = None
+        for line in open(path):
+            if line.startswith("traffic_record:"):
+                rec = json.loads(line.split(":", 1)[1])
+        sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("source_sha256") != sha:
+        return None
+    return rec
 
 
 def upload(x, device="cuda"):
@@ -204,6 +224,10 @@ def main():
     select_bytes = 4 * i.num_q_heads * i.score_elems_per_head + \
         4 * i.num_q_heads * i.total_blocks * (i.kmax + 1)
 
+    trec = traffic_record(name)
+    # Q, K, V read once, O and LSE written once
+    attn_bytes_min = i.total_tokens * (i.num_q_heads + 2 * i.num_kv_heads) * i.head_dim * esz + \
+        i.total_tokens * i.num_q_heads * i.head_dim * out_dtype.itemsize + 4 * i.total_tokens * i.num_q_heads
     result = {
         "metric": METRIC,
         "value": round(step_ms, 4),
@@ -224,7 +248,10 @@ def main():
                    "executed_blocks_per_head": i.executed_blocks_per_head},
         "roofline": {"bound": "mfma", "kernel": "attn", "achieved": round(achieved, 2),
                      "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
-                     "traffic": None,
+                     "traffic": (None if trec is None
+                                 else trec["fetch_bytes"] + trec["write_bytes"]),
+                     "traffic_detail": trec,
+                     "algorithmic_bytes_min": attn_bytes_min,
                      "flop_per_launch": flops_alg,
                      "avg_launch_ms": round(attn_ms, 4)},
         "stages_ms": {n: round(stage_ms[n], 4) for n in names},
