@@ -1,9 +1,11 @@
-// Output-Aware Metric on pooled blocks (gist.science/es 2.B and
-// gist.science/fr 2.B: routing relevance of a key block combined with the
-// magnitude of its values), in the multiplicative form
-//   m_ij = softmax_{j <= i}(qbar_i . kbar_j / sqrt(d)) * vnorm_j
-// which orders key blocks of a row exactly like the pages' additive form
-// s_ij + beta * log ||V_j||^2 with beta = 1/2.
+// Block metric on pooled blocks (gist.science/es 2.B and gist.science/fr
+// 2.B: routing relevance of a key block combined with the magnitude of its
+// values).  Three forms, chosen by the plan:
+//   output-aware  m_ij = softmax_{j <= i}(s_ij) * vnorm_j
+//   additive      m_ij = s_ij + beta * max(0, log vnorm_j^2)
+//   routing       m_ij = softmax_{j <= i}(s_ij)
+// with s_ij = qbar_i . kbar_j / sqrt(d).  Inside a row the output-aware form
+// orders key blocks exactly like the additive one with beta = 1/2.
 //
 // One workgroup owns 32 consecutive query-block rows of one (query head,
 // sequence); its 8 wavefronts split the causal key blocks 32 at a time
@@ -11,9 +13,11 @@
 // products are an f32 GEMM on the matrix cores (v_mfma_f32_32x32x2_f32,
 // computing the transposed tile keys x queries so that each lane holds one
 // query row's values and row statistics never leave the lane pair l, l^32).
-// Pass 1 keeps an online row max / sum (and the scaled logits, in registers
-// or parked in the output); pass 2 writes exp(x - max) / sum * vnorm.  f32
-// throughout; exponentials use the hardware exp2 (relative error ~1e-6).
+// Softmax forms: pass 1 keeps an online row max / sum (and the scaled
+// logits, in registers or parked in the output); pass 2 writes
+// exp(x - max) / sum (* vnorm).  The additive form needs no row statistics
+// and is written in pass 1.  f32 throughout; exponentials use the hardware
+// exp2 (relative error ~1e-6).
 #include "stem_device.h"
 
 namespace stem {
@@ -26,11 +30,12 @@ struct ScoreArgs {
   int32_t Hq, Hkv, nbT, num_seqs;
   int64_t per_head;
   float scale;
+  float beta;
 };
 
 constexpr int kScoreWaves = 8;
 
-template <int D>
+template <int D, int MODE>
 __global__ __launch_bounds__(64 * kScoreWaves) void score_kernel(ScoreArgs a) {
   constexpr int HALF = D / 2;
   __shared__ float st_m[kScoreWaves][64];
@@ -101,6 +106,19 @@ __global__ __launch_bounds__(64 * kScoreWaves) void score_kernel(ScoreArgs a) {
         acc = __builtin_amdgcn_mfma_f32_32x32x2f32(kcur[c][e], qv[4 * c + e], acc, 0, 0, 0);
     const int j0 = jt * 32;
     // acc[r] = logit(key j0 + 8(r/4) + 4hi + r%4, query qi)
+    if constexpr (MODE == STEM_METRIC_ADDITIVE) {
+      const float *w = a.vnorm + int64_t(g) * a.nbT + b0;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int j = j0 + 8 * (r >> 2) + 4 * hi + (r & 3);
+        if (qvalid && j <= qi) {
+          // log(w^2) as 2 log w: no overflow for large w; log 0 = -inf -> 0
+          const float bonus = fmaxf(0.f, 2.f * logf(w[j]));
+          a.scores[rowbase + j] = fmaf(a.beta, bonus, acc[r] * a.scale);
+        }
+      }
+      continue;
+    }
     float bm = -INFINITY;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
@@ -128,6 +146,7 @@ __global__ __launch_bounds__(64 * kScoreWaves) void score_kernel(ScoreArgs a) {
       }
     }
   }
+  if constexpr (MODE == STEM_METRIC_ADDITIVE) return;
   // combine the statistics of the 8 wavefronts and of the two lanes that
   // share a query row
   st_m[wv][lane] = mrun;
@@ -144,7 +163,7 @@ __global__ __launch_bounds__(64 * kScoreWaves) void score_kernel(ScoreArgs a) {
     if (m1 != -INFINITY) L += st_l[v][lane ^ 32] * __expf(m1 - M);
   }
   if (!qvalid) return;
-  // pass 2: write this wavefront's values as exp(x - M) / L * vnorm
+  // pass 2: write this wavefront's values as exp(x - M) / L (* vnorm)
   const float invL = 1.0f / L;
   const float *w = a.vnorm + int64_t(g) * a.nbT + b0;
   slot = 0;
@@ -161,7 +180,8 @@ __global__ __launch_bounds__(64 * kScoreWaves) void score_kernel(ScoreArgs a) {
       const int j = j0 + 8 * (r >> 2) + 4 * hi + (r & 3);
       if (j <= qi) {
         const float v = slot < kKeep ? x[r] : a.scores[rowbase + j];
-        a.scores[rowbase + j] = __expf(v - M) * invL * w[j];
+        const float p = __expf(v - M) * invL;
+        a.scores[rowbase + j] = MODE == STEM_METRIC_ROUTING ? p : p * w[j];
       }
     }
   }
@@ -184,11 +204,26 @@ hipError_t launch_score(const stem_plan_info &in, PlanDev pd, const float *qbar,
   a.num_seqs = in.num_seqs;
   a.per_head = in.score_elems_per_head;
   a.scale = 1.0f / sqrtf(static_cast<float>(in.head_dim));
+  a.beta = static_cast<float>(in.beta);
   dim3 grid(static_cast<unsigned>(tiles), in.num_q_heads);
-  if (in.head_dim == 128)
-    hipLaunchKernelGGL((score_kernel<128>), grid, dim3(64 * kScoreWaves), 0, st, a);
-  else
-    hipLaunchKernelGGL((score_kernel<64>), grid, dim3(64 * kScoreWaves), 0, st, a);
+  const dim3 block(64 * kScoreWaves);
+  const bool d128 = in.head_dim == 128;
+  switch (in.metric_mode) {
+    case STEM_METRIC_ADDITIVE:
+      if (d128) hipLaunchKernelGGL((score_kernel<128, STEM_METRIC_ADDITIVE>), grid, block, 0, st, a);
+      else hipLaunchKernelGGL((score_kernel<64, STEM_METRIC_ADDITIVE>), grid, block, 0, st, a);
+      break;
+    case STEM_METRIC_ROUTING:
+      if (d128) hipLaunchKernelGGL((score_kernel<128, STEM_METRIC_ROUTING>), grid, block, 0, st, a);
+      else hipLaunchKernelGGL((score_kernel<64, STEM_METRIC_ROUTING>), grid, block, 0, st, a);
+      break;
+    default:
+      if (d128)
+        hipLaunchKernelGGL((score_kernel<128, STEM_METRIC_OUTPUT_AWARE>), grid, block, 0, st, a);
+      else
+        hipLaunchKernelGGL((score_kernel<64, STEM_METRIC_OUTPUT_AWARE>), grid, block, 0, st, a);
+      break;
+  }
   return hipGetLastError();
 }
 

@@ -19,6 +19,8 @@ int check_info(const stem_plan_info *in, const void *plan_dev) {
   if (in->block != 64 && in->block != 128) return STEM_EUNSUPPORTED;
   if (in->dtype != STEM_F32 && in->dtype != STEM_BF16) return STEM_EUNSUPPORTED;
   if (in->total_blocks < 0 || in->total_tokens < 0) return STEM_EINVAL;
+  if (in->metric_mode < STEM_METRIC_OUTPUT_AWARE || in->metric_mode > STEM_METRIC_ROUTING)
+    return STEM_EINVAL;
   if (in->total_blocks > 0 && (!plan_dev || !aligned(plan_dev, 16))) return STEM_EINVAL;
   return STEM_OK;
 }

@@ -18,19 +18,35 @@ int64_t align16(int64_t x) { return (x + 15) & ~int64_t(15); }
 
 int64_t tri(int64_t n) { return n * (n + 1) / 2; }
 
-// Budget of local query block i (gist.science/es 2.A and gist.science/fr
-// 2.A: position-dependent top-k, high for early positions, decaying later;
-// exponential shape as in the shd-paper.top method detail).  Evaluated in
-// double precision with the C library exp and ceil.
-int32_t budget_of(int64_t i, const stem_params &p) {
+// Number of blocks chosen by the metric for local query block i of a
+// sequence with nb blocks, before the k_min floor and the causal cap
+// (gist.science/es 2.A and gist.science/fr 2.A: position-dependent top-k,
+// high for early positions and decaying later).  Evaluated in double
+// precision with the C library exp and ceil; every product and sum is its
+// own statement so that no fused multiply-add changes the rounding.
+double kdyn_raw(int64_t i, int64_t nb, const stem_params &p) {
+  if (p.budget_mode == STEM_BUDGET_LINEAR) {
+    const double f = nb <= 1 ? 0.0 : static_cast<double>(i) / static_cast<double>(nb - 1);
+    const double a = p.k_start * (1.0 - f);
+    const double b = p.mu * p.k_start;
+    const double c = b * f;
+    const double x = a + c;
+    return std::ceil(x);
+  }
+  const double e = std::exp(-static_cast<double>(i) / p.tau);
+  const double x = p.rho0 * e * static_cast<double>(i + 1);
+  return std::ceil(x);
+}
+
+int32_t budget_of(int64_t i, int64_t nb, const stem_params &p) {
   if (i < p.sink_blocks) return static_cast<int32_t>(i + 1);
-  const double x = p.rho0 * std::exp(-static_cast<double>(i) / p.tau) *
-                   static_cast<double>(i + 1);
-  const double c = std::ceil(x);
+  const double c = kdyn_raw(i, nb, p);
   // k_dyn = max(k_min, ceil(x)), then k_i = min(i + 1, S + 1 + k_dyn)
   int64_t kdyn;
   if (c >= static_cast<double>(i + 1)) {
     kdyn = i + 1;  // saturates below anyway; avoids overflow for huge x
+  } else if (c <= 0.0) {
+    kdyn = 0;
   } else {
     kdyn = static_cast<int64_t>(c);
   }
@@ -51,8 +67,19 @@ extern "C" int stem_plan(const stem_problem *pr, const stem_params *pa,
   if (pr->head_dim != 64 && pr->head_dim != 128) return STEM_EUNSUPPORTED;
   if (pr->block != 64 && pr->block != 128) return STEM_EUNSUPPORTED;
   if (pa->sink_blocks < 0 || pa->k_min < 0) return STEM_EINVAL;
-  if (!std::isfinite(pa->rho0) || pa->rho0 < 0.0) return STEM_EINVAL;
-  if (!std::isfinite(pa->tau) || !(pa->tau > 0.0)) return STEM_EINVAL;
+  if (pa->budget_mode == STEM_BUDGET_EXP) {
+    if (!std::isfinite(pa->rho0) || pa->rho0 < 0.0) return STEM_EINVAL;
+    if (!std::isfinite(pa->tau) || !(pa->tau > 0.0)) return STEM_EINVAL;
+  } else if (pa->budget_mode == STEM_BUDGET_LINEAR) {
+    if (!std::isfinite(pa->k_start) || pa->k_start < 0.0) return STEM_EINVAL;
+    if (!(pa->mu >= 0.0 && pa->mu <= 1.0)) return STEM_EINVAL;
+  } else {
+    return STEM_EINVAL;
+  }
+  if (pa->metric_mode != STEM_METRIC_OUTPUT_AWARE && pa->metric_mode != STEM_METRIC_ADDITIVE &&
+      pa->metric_mode != STEM_METRIC_ROUTING)
+    return STEM_EINVAL;
+  if (!std::isfinite(pa->beta) || pa->beta < 0.0) return STEM_EINVAL;
 
   const int32_t ns = pr->num_seqs;
   const int32_t *cu = pr->cu_seqlens;
@@ -81,7 +108,7 @@ extern "C" int stem_plan(const stem_problem *pr, const stem_params *pa,
     for (int32_t s = 0; s < ns; ++s) {
       const int64_t nb = (int64_t(cu[s + 1]) - cu[s] + pr->block - 1) / pr->block;
       for (int64_t i = 0; i < nb; ++i, ++b) {
-        budget[b] = budget_of(i, *pa);
+        budget[b] = budget_of(i, nb, *pa);
         executed += budget[b];
         kmax = std::max(kmax, budget[b]);
       }
@@ -100,6 +127,8 @@ extern "C" int stem_plan(const stem_problem *pr, const stem_params *pa,
   in.sink_blocks = pa->sink_blocks;
   in.kmax = kmax;
   in.max_seq_blocks = max_nb;
+  in.metric_mode = pa->metric_mode;
+  in.beta = pa->beta;
   in.total_tokens = T;
   in.total_blocks = nbT;
   in.score_elems_per_head = tri_total;

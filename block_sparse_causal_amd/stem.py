@@ -20,6 +20,11 @@ _lib = None
 STEM_OK, STEM_EINVAL, STEM_EUNSUPPORTED, STEM_EHIP, STEM_ESPACE = 0, -1, -2, -3, -4
 STEM_F32, STEM_BF16 = 0, 1
 STEM_VNORM_MEAN, STEM_VNORM_MAX = 0, 1
+STEM_BUDGET_EXP, STEM_BUDGET_LINEAR = 0, 1
+STEM_METRIC_OUTPUT_AWARE, STEM_METRIC_ADDITIVE, STEM_METRIC_ROUTING = 0, 1, 2
+BUDGET_MODES = {"exp": STEM_BUDGET_EXP, "linear": STEM_BUDGET_LINEAR}
+METRICS = {"output_aware": STEM_METRIC_OUTPUT_AWARE, "additive": STEM_METRIC_ADDITIVE,
+           "routing": STEM_METRIC_ROUTING}
 STEM_PLAN_MAGIC = 0x5354454D
 
 DTYPES = {"f32": STEM_F32, "bf16": STEM_BF16}
@@ -45,7 +50,12 @@ class stem_params(ctypes.Structure):
     _fields_ = [("sink_blocks", ctypes.c_int32),
                 ("k_min", ctypes.c_int32),
                 ("rho0", ctypes.c_double),
-                ("tau", ctypes.c_double)]
+                ("tau", ctypes.c_double),
+                ("budget_mode", ctypes.c_int32),
+                ("metric_mode", ctypes.c_int32),
+                ("k_start", ctypes.c_double),
+                ("mu", ctypes.c_double),
+                ("beta", ctypes.c_double)]
 
 
 class stem_plan_info(ctypes.Structure):
@@ -59,6 +69,9 @@ class stem_plan_info(ctypes.Structure):
                 ("sink_blocks", ctypes.c_int32),
                 ("kmax", ctypes.c_int32),
                 ("max_seq_blocks", ctypes.c_int32),
+                ("metric_mode", ctypes.c_int32),
+                ("reserved", ctypes.c_int32),
+                ("beta", ctypes.c_double),
                 ("total_tokens", ctypes.c_int64),
                 ("total_blocks", ctypes.c_int64),
                 ("score_elems_per_head", ctypes.c_int64),
@@ -163,11 +176,14 @@ class Plan:
 
 def stem_plan(cu_seqlens: Sequence[int], num_q_heads: int, num_kv_heads: int, head_dim: int,
               block: int, dtype: str, sink_blocks: int, k_min: int, rho0: float,
-              tau: float) -> Plan:
+              tau: float, budget_mode: str = "exp", k_start: float = 0.0, mu: float = 0.0,
+              metric: str = "output_aware", beta: float = 0.5) -> Plan:
     cu = np.ascontiguousarray(np.asarray(cu_seqlens, dtype=np.int32))
     pr = stem_problem(len(cu) - 1, cu.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
                       num_q_heads, num_kv_heads, head_dim, block, DTYPES.get(dtype, 99))
-    pa = stem_params(sink_blocks, k_min, float(rho0), float(tau))
+    pa = stem_params(sink_blocks, k_min, float(rho0), float(tau),
+                     BUDGET_MODES.get(budget_mode, 99), METRICS.get(metric, 99),
+                     float(k_start), float(mu), float(beta))
     info = stem_plan_info()
     L = lib()
     _check("stem_plan", L.stem_plan(ctypes.byref(pr), ctypes.byref(pa), ctypes.byref(info),
@@ -182,7 +198,8 @@ def plan_for(workload, **override) -> Plan:
     """stem_plan for a synthetic.Workload (parameters may be overridden)."""
     w = workload.replace(**override) if override else workload
     return stem_plan(w.cu_seqlens, w.num_q_heads, w.num_kv_heads, w.head_dim, w.block,
-                     w.dtype, w.sink_blocks, w.k_min, w.rho0, w.tau)
+                     w.dtype, w.sink_blocks, w.k_min, w.rho0, w.tau, w.budget_mode,
+                     w.k_start, w.mu, w.metric, w.beta)
 
 
 # ---------------------------------------------------------------- device calls

@@ -50,6 +50,11 @@ class Workload:
     rho0: float
     tau: float            # decay length, in blocks
     seed: int = 0
+    budget_mode: str = "exp"          # "exp" (rho0, tau) or "linear" (k_start, mu)
+    k_start: float = 0.0              # linear budget: dynamic blocks at the first row
+    mu: float = 0.0                   # linear budget: k_end / k_start
+    metric: str = "output_aware"      # "output_aware", "additive" or "routing"
+    beta: float = 0.5                 # additive metric weight
 
     @property
     def total_tokens(self) -> int:
@@ -184,9 +189,10 @@ def custom(seqlens: List[int], num_q_heads: int, num_kv_heads: int,
            head_dim: int, dtype: str, block: int, *, sink_blocks: int = 2,
            k_min: int = 4, rho0: float = 0.5, tau: float = 8.0,
            rope_theta: Optional[float] = 5.0e5, seed: int = 7,
-           name: str = "custom") -> Workload:
-    """A small workload of the same distribution, for tests."""
+           name: str = "custom", **params) -> Workload:
+    """A small workload of the same distribution, for tests (``params`` sets
+    budget_mode, k_start, mu, metric or beta)."""
     return Workload(name, tuple(int(x) for x in seqlens), num_q_heads,
                     num_kv_heads, head_dim, dtype, rope_theta, block,
-                    sink_blocks, k_min, float(rho0), float(tau), seed)
+                    sink_blocks, k_min, float(rho0), float(tau), seed, **params)
 

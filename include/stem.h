@@ -54,6 +54,16 @@ typedef enum {
 
 typedef enum { STEM_F32 = 0, STEM_BF16 = 1 } stem_dtype;
 
+/* Shape of the position-dependent budget (see stem_params). */
+typedef enum { STEM_BUDGET_EXP = 0, STEM_BUDGET_LINEAR = 1 } stem_budget_mode;
+
+/* Which block metric stem_score writes (see stem_score). */
+typedef enum {
+  STEM_METRIC_OUTPUT_AWARE = 0,  /* softmax_j(s_ij) * w_j                      */
+  STEM_METRIC_ADDITIVE = 1,      /* s_ij + beta * max(0, log(w_j^2))            */
+  STEM_METRIC_ROUTING = 2        /* softmax_j(s_ij): attention score alone      */
+} stem_metric_mode;
+
 /* How the block V magnitude is pooled (the method's metric needs one value
  * per key block).  MEAN: mean over the block's tokens of ||v_t||_2.
  * MAX: the maximum of ||v_t||_2 over the block's tokens. */
@@ -71,20 +81,30 @@ typedef struct stem_problem {
 } stem_problem;
 
 /* Token Position-Decay budget (gist.science/es 2.A, gist.science/fr 2.A: a
- * high budget for early query positions decaying to a lower one later;
- * the decay shape used here is the exponential one of the shd-paper.top
- * method detail).  For local query block i of a sequence:
- *   k_dyn(i) = max(k_min, ceil(rho0 * exp(-i / tau) * (i + 1)))   (fp64)
- *   k_i      = i + 1                              if i < sink_blocks
- *            = min(i + 1, sink_blocks + 1 + k_dyn(i)) otherwise
+ * high budget for early query positions decaying to a lower one later).
+ * For local query block i of a sequence with nb blocks, k_dyn(i) is
+ *   STEM_BUDGET_EXP (decay shape of the shd-paper.top method detail):
+ *     max(k_min, ceil(rho0 * exp(-i / tau) * (i + 1)))
+ *   STEM_BUDGET_LINEAR (the gist.science pages' linear interpolation from
+ *   k_start to k_end = mu * k_start over the sequence's query blocks):
+ *     max(k_min, ceil(k_start * (1 - f) + mu * k_start * f)), f = i / (nb - 1)
+ * evaluated in fp64, and the kept count is
+ *   k_i = i + 1                                if i < sink_blocks
+ *       = min(i + 1, sink_blocks + 1 + k_dyn(i)) otherwise
  * so the first sink_blocks blocks (initial tokens are the anchors every
- * later token aggregates, gist.science/es section 1) and the diagonal
- * block are always kept and k_dyn further blocks are chosen by the metric. */
+ * later token aggregates, gist.science/es section 1) and the diagonal block
+ * are always kept and k_dyn further blocks are chosen by the metric.
+ * rho0 = 0 (or mu = 1) gives a uniform budget. */
 typedef struct stem_params {
   int32_t sink_blocks;          /* S >= 0 */
   int32_t k_min;                /* >= 0 */
-  double rho0;                  /* >= 0, finite */
-  double tau;                   /* > 0, in blocks */
+  double rho0;                  /* >= 0, finite (EXP) */
+  double tau;                   /* > 0, in blocks (EXP) */
+  int32_t budget_mode;          /* stem_budget_mode */
+  int32_t metric_mode;          /* stem_metric_mode */
+  double k_start;               /* >= 0, finite (LINEAR), in blocks */
+  double mu;                    /* in [0, 1] (LINEAR) */
+  double beta;                  /* >= 0, finite (ADDITIVE metric) */
 } stem_params;
 
 /* Sizes and offsets computed by stem_plan.  The caller passes it back,
@@ -95,6 +115,9 @@ typedef struct stem_plan_info {
   int32_t sink_blocks;
   int32_t kmax;                     /* max_i k_i: third extent of idx */
   int32_t max_seq_blocks;           /* max_s ceil(len_s / B) */
+  int32_t metric_mode;              /* stem_metric_mode */
+  int32_t reserved;
+  double beta;                      /* ADDITIVE metric weight */
   int64_t total_tokens;             /* T */
   int64_t total_blocks;             /* nbT = sum_s ceil(len_s / B) */
   int64_t score_elems_per_head;     /* sum_s nb_s (nb_s + 1) / 2 */
@@ -133,9 +156,13 @@ int stem_pool(const stem_plan_info *info, const void *plan_dev,
 /* stem_score - Output-Aware Metric per (query block, causal key block)
  * (gist.science/es 2.B; gist.science/fr 2.B: routing relevance combined
  * with the magnitude of the values).  For query head h, sequence s, local
- * query block i and local key block j <= i:
- *   s_ij = qbar_i . kbar_j / sqrt(d)
- *   m_ij = softmax over j in [0, i] of s_ij, times vnorm_j
+ * query block i and local key block j <= i, with s_ij = qbar_i . kbar_j / sqrt(d):
+ *   OUTPUT_AWARE  m_ij = softmax over j in [0, i] of s_ij, times vnorm_j
+ *   ADDITIVE      m_ij = s_ij + beta * max(0, log(vnorm_j^2))  (the pages'
+ *                 displayed formula, gist.science/es 2.B equation)
+ *   ROUTING       m_ij = softmax over j in [0, i] of s_ij (routing alone,
+ *                 the criterion the pages argue against, es section 1)
+ * (mode and beta from the plan)
  * scores is f32 [Hq, score_elems_per_head]: for each head the sequences'
  * lower triangles one after another (plan off_tri), row i of a sequence
  * starting i (i + 1) / 2 elements into its triangle. */

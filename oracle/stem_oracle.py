@@ -129,15 +129,23 @@ def pool_vnorm(v: np.ndarray, cu_seqlens: Sequence[int], block: int,
 # [fr] 2.B): routing relevance of the block times the magnitude of its values
 
 
+METRICS = ("output_aware", "additive", "routing")
+
+
 def score(qbar: np.ndarray, kbar: np.ndarray, w: np.ndarray,
-          cu_blocks: np.ndarray, head_dim: int) -> np.ndarray:
+          cu_blocks: np.ndarray, head_dim: int, metric: str = "output_aware",
+          beta: float = 0.5) -> np.ndarray:
     """Packed lower-triangular metric m [Hq, tri_total] (float64).
 
     For query head h (KV head g = h // (Hq/Hkv)), sequence s and local query
     block i, the row holds, for j = 0..i (local key blocks):
         s_ij = qbar_i . kbar_j / sqrt(head_dim)
         p_ij = exp(s_ij - max_j s) / sum_j exp(s_ij - max_j s)
-        m_ij = p_ij * w_j
+        m_ij = p_ij * w_j                         metric "output_aware"
+             = s_ij + beta * max(0, log(w_j^2))   metric "additive" (the
+               displayed formula of [es] 2.B and [fr] 2.B)
+             = p_ij                               metric "routing" (attention
+               score alone, the criterion [es] 1 argues against)
     """
     Hq = qbar.shape[0]
     offs, total = score_offsets(cu_blocks)
@@ -148,20 +156,30 @@ def score(qbar: np.ndarray, kbar: np.ndarray, w: np.ndarray,
             for i in range(nb):
                 row0 = int(offs[s]) + tri(i)
                 out[h, row0:row0 + i + 1] = score_row_values(qbar, kbar, w, cu_blocks,
-                                                             head_dim, h, s, i)
+                                                             head_dim, h, s, i,
+                                                             metric, beta)
     return out
 
 
 def score_row_values(qbar: np.ndarray, kbar: np.ndarray, w: np.ndarray,
-                     cu_blocks: np.ndarray, head_dim: int, h: int, s: int, i: int) -> np.ndarray:
+                     cu_blocks: np.ndarray, head_dim: int, h: int, s: int, i: int,
+                     metric: str = "output_aware", beta: float = 0.5) -> np.ndarray:
     """One row of the metric: m_i0 .. m_ii for query head h, sequence s,
     local query block i (see score)."""
+    if metric not in METRICS:
+        raise ValueError(metric)
     g = h // (qbar.shape[0] // kbar.shape[0])
     b0 = int(cu_blocks[s])
     logits = kbar[g, b0:b0 + i + 1, :] @ qbar[h, b0 + i, :] * (1.0 / math.sqrt(head_dim))
+    wj = w[g, b0:b0 + i + 1].astype(np.float64)
+    if metric == "additive":
+        # log(0) = -inf, so a block of zero values gets no bonus
+        with np.errstate(divide="ignore"):
+            lw2 = np.log(wj * wj)
+        return logits + beta * np.maximum(0.0, lw2)
     p = np.exp(logits - logits.max())
     p /= p.sum()
-    return p * w[g, b0:b0 + i + 1]
+    return p if metric == "routing" else p * wj
 
 
 def score_row(m: np.ndarray, cu_blocks: np.ndarray, h: int, s: int, i: int) -> np.ndarray:
@@ -195,18 +213,23 @@ def budget(nb: int, sink_blocks: int, k_min: int, rho0: float, tau: float) -> np
     return out
 
 
-def budget_linear(nb: int, sink_blocks: int, k_start: int, mu: float) -> np.ndarray:
+def budget_linear(nb: int, sink_blocks: int, k_min: int, k_start: float,
+                  mu: float) -> np.ndarray:
     """The pages' linear form ([es] 2.A, [fr] 2.A): the number of dynamically
-    chosen blocks goes linearly from k_start at the first query block to
-    mu*k_start at the last, rounded up; sinks and diagonal are added on top."""
+    chosen blocks goes linearly from k_start at the first query block of the
+    sequence to k_end = mu*k_start at its last, rounded up and floored at
+    k_min; sinks and diagonal are added on top and the causal count caps it:
+        f        = i / (nb - 1)            (0 when nb = 1)
+        k_dyn(i) = max(k_min, ceil(k_start*(1-f) + mu*k_start*f))
+        k_i      = i+1 if i < S, else min(i+1, S + 1 + k_dyn(i))"""
     out = np.zeros(nb, dtype=np.int64)
     for i in range(nb):
         if i < sink_blocks:
             out[i] = i + 1
             continue
         frac = 0.0 if nb <= 1 else i / (nb - 1)
-        kd = int(math.ceil(k_start * (1.0 - frac) + mu * k_start * frac))
-        out[i] = min(i + 1, sink_blocks + 1 + max(kd, 0))
+        kd = max(k_min, int(math.ceil(k_start * (1.0 - frac) + mu * k_start * frac)))
+        out[i] = min(i + 1, sink_blocks + 1 + kd)
     return out
 
 
@@ -368,15 +391,25 @@ def dense_causal_attn(q: np.ndarray, k: np.ndarray, v: np.ndarray, cu_seqlens):
 
 
 def budgets_for(cu_blocks: np.ndarray, sink_blocks: int, k_min: int,
-                rho0: float, tau: float) -> np.ndarray:
-    """Per-global-block budget table, each sequence restarting at i = 0."""
-    parts = [budget(int(cu_blocks[s + 1] - cu_blocks[s]), sink_blocks, k_min, rho0, tau)
-             for s in range(len(cu_blocks) - 1)]
+                rho0: float, tau: float, mode: str = "exp", k_start: float = 0.0,
+                mu: float = 0.0) -> np.ndarray:
+    """Per-global-block budget table, each sequence restarting at i = 0;
+    mode "exp" uses budget, mode "linear" uses budget_linear."""
+    if mode == "exp":
+        parts = [budget(int(cu_blocks[s + 1] - cu_blocks[s]), sink_blocks, k_min, rho0, tau)
+                 for s in range(len(cu_blocks) - 1)]
+    elif mode == "linear":
+        parts = [budget_linear(int(cu_blocks[s + 1] - cu_blocks[s]), sink_blocks, k_min,
+                               k_start, mu)
+                 for s in range(len(cu_blocks) - 1)]
+    else:
+        raise ValueError(mode)
     return np.concatenate(parts) if parts else np.zeros(0, np.int64)
 
 
 def prefill(q, k, v, cu_seqlens, block, sink_blocks, k_min, rho0, tau,
-            vnorm_mode: str = "mean"):
+            vnorm_mode: str = "mean", metric: str = "output_aware", beta: float = 0.5,
+            budget_mode: str = "exp", k_start: float = 0.0, mu: float = 0.0):
     """pool -> score -> budget -> select -> attention.  Returns a dict of
     every intermediate (float64 / int)."""
     d = q.shape[2]
@@ -384,8 +417,8 @@ def prefill(q, k, v, cu_seqlens, block, sink_blocks, k_min, rho0, tau,
     qbar = pool_mean(q, cu_seqlens, block)
     kbar = pool_mean(k, cu_seqlens, block)
     w = pool_vnorm(v, cu_seqlens, block, vnorm_mode)
-    m = score(qbar, kbar, w, cub, d)
-    bud = budgets_for(cub, sink_blocks, k_min, rho0, tau)
+    m = score(qbar, kbar, w, cub, d, metric, beta)
+    bud = budgets_for(cub, sink_blocks, k_min, rho0, tau, budget_mode, k_start, mu)
     idx, cnt = select(m, cub, bud, sink_blocks)
     o, lse = sparse_attn(q, k, v, idx, cnt, cu_seqlens, block)
     return dict(qbar=qbar, kbar=kbar, w=w, m=m, budget=bud, idx=idx,

@@ -82,11 +82,16 @@ def check_out(got: np.ndarray, ref: np.ndarray, dtype: str, out_dtype: str, what
     return float(err.max())
 
 
-def check_scores(got: np.ndarray, ref: np.ndarray, dtype: str, what: str):
+def check_scores(got: np.ndarray, ref: np.ndarray, dtype: str, what: str,
+                 metric: str = "output_aware"):
+    """Softmax metrics are positive and checked relative to each value; the
+    additive metric is a logit that crosses zero, so its relative check uses
+    max(|ref|, 1) (an absolute bound below 1)."""
     t = TOL[dtype]
     err = np.abs(got - ref)
     assert err.max() <= t["score"], f"{what}: max abs err {err.max():.3g}"
-    rel = err / np.maximum(np.abs(ref), 1e-30)
+    floor = 1.0 if metric == "additive" else 1e-30
+    rel = err / np.maximum(np.abs(ref), floor)
     assert rel.max() <= t["score_rel"], f"{what}: max rel err {rel.max():.3g}"
     return float(err.max()), float(rel.max())
 

@@ -31,9 +31,13 @@ def test_library_exports_every_declared_symbol():
 
 def test_struct_layouts_match_header():
     # offsets follow C layout rules; a mismatch would corrupt every call
-    assert ctypes.sizeof(stem.stem_params) == 24
-    assert stem.stem_plan_info.total_tokens.offset == 40
-    assert ctypes.sizeof(stem.stem_plan_info) == 40 + 11 * 8
+    assert ctypes.sizeof(stem.stem_params) == 56
+    assert stem.stem_params.budget_mode.offset == 24
+    assert stem.stem_params.beta.offset == 48
+    assert stem.stem_plan_info.metric_mode.offset == 40
+    assert stem.stem_plan_info.beta.offset == 48
+    assert stem.stem_plan_info.total_tokens.offset == 56
+    assert ctypes.sizeof(stem.stem_plan_info) == 56 + 11 * 8
     assert stem.stem_problem.cu_seqlens.offset == 8
 
 
@@ -70,6 +74,30 @@ def test_plan_budget_random_parameters(seed):
     np.testing.assert_array_equal(p.budget, O.budgets_for(cub, S, k_min, rho0, tau))
 
 
+@pytest.mark.parametrize("seed", range(20))
+def test_plan_linear_budget_random_parameters(seed):
+    r = np.random.default_rng(100 + seed)
+    seqlens = list(r.integers(0, 4000, size=r.integers(1, 5)))
+    block = int(r.choice([64, 128]))
+    S = int(r.integers(0, 5))
+    k_min = int(r.integers(0, 6))
+    k_start = float(r.choice([r.uniform(0, 40), 16.0, 0.0, 7.5]))
+    mu = float(r.choice([r.uniform(0, 1), 0.0, 1.0, 0.3]))
+    cu = np.concatenate([[0], np.cumsum(seqlens)])
+    p = stem.stem_plan(cu, 4, 2, 64, block, "bf16", S, k_min, 0.0, 1.0,
+                       budget_mode="linear", k_start=k_start, mu=mu)
+    cub = O.block_layout(cu, block)
+    np.testing.assert_array_equal(
+        p.budget, O.budgets_for(cub, S, k_min, 0.0, 1.0, "linear", k_start, mu))
+
+
+def test_plan_carries_metric_mode_and_beta():
+    for name, code in stem.METRICS.items():
+        p = stem.stem_plan([0, 512], 2, 1, 64, 64, "f32", 1, 1, 0.5, 4.0, metric=name,
+                           beta=0.25)
+        assert p.info.metric_mode == code and p.info.beta == 0.25
+
+
 def test_plan_ragged_and_empty_sequences():
     cu = [0, 0, 1, 1, 130, 130]
     p = stem.stem_plan(cu, 2, 1, 64, 64, "f32", 1, 1, 0.5, 4.0)
@@ -90,7 +118,7 @@ def test_plan_rejects_bad_arguments():
 
     def bad(**kw):
         a = dict(ok); a.update(kw)
-        return _status(stem.stem_plan, *a.values())
+        return _status(lambda: stem.stem_plan(**a))
 
     assert bad(num_kv_heads=3) == stem.STEM_EINVAL
     assert bad(num_q_heads=0) == stem.STEM_EINVAL
@@ -106,6 +134,17 @@ def test_plan_rejects_bad_arguments():
     assert bad(tau=0.0) == stem.STEM_EINVAL
     assert bad(tau=float("inf")) == stem.STEM_EINVAL
     assert bad(cu_seqlens=[0, 64 * 4097]) == stem.STEM_EUNSUPPORTED
+    assert bad(budget_mode="cosine") == stem.STEM_EINVAL
+    assert bad(metric="oam") == stem.STEM_EINVAL
+    assert bad(metric="additive", beta=-1.0) == stem.STEM_EINVAL
+    assert bad(beta=float("nan")) == stem.STEM_EINVAL
+    assert bad(budget_mode="linear", k_start=-1.0) == stem.STEM_EINVAL
+    assert bad(budget_mode="linear", k_start=float("inf")) == stem.STEM_EINVAL
+    assert bad(budget_mode="linear", k_start=4.0, mu=1.5) == stem.STEM_EINVAL
+    assert bad(budget_mode="linear", k_start=4.0, mu=float("nan")) == stem.STEM_EINVAL
+    # the exponential parameters are not checked in linear mode, and vice versa
+    assert stem.stem_plan(*dict(ok, tau=0.0).values(), budget_mode="linear", k_start=2.0,
+                          mu=0.5).info.kmax >= 1
 
 
 def test_plan_reports_small_buffer():

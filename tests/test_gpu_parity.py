@@ -47,14 +47,16 @@ SMALL = {
 def _full_check(r: H.GpuRun):
     w = r.w
     ref = O.prefill(r.x.q, r.x.k, r.x.v, w.cu_seqlens, w.block, w.sink_blocks, w.k_min,
-                    w.rho0, w.tau)
+                    w.rho0, w.tau, metric=w.metric, beta=w.beta, budget_mode=w.budget_mode,
+                    k_start=w.k_start, mu=w.mu)
+    np.testing.assert_array_equal(r.budget, ref["budget"])
     t = H.TOL[w.dtype]
     # stage 1: pooled values
     np.testing.assert_allclose(r.qbar, ref["qbar"], rtol=t["pool"], atol=t["pool"])
     np.testing.assert_allclose(r.kbar, ref["kbar"], rtol=t["pool"], atol=t["pool"])
     np.testing.assert_allclose(r.vnorm, ref["w"], rtol=t["pool"], atol=t["pool"])
     # metric
-    H.check_scores(r.scores, ref["m"], w.dtype, "scores")
+    H.check_scores(r.scores, ref["m"], w.dtype, "scores", w.metric)
     # selection, on the GPU's own scores: bit-exact
     H.select_rows_crossfed(r, H.all_rows(r))
     # attention with the GPU's lists: every row
@@ -91,6 +93,35 @@ def test_bf16_output_mode(name):
     r = H.GpuRun(SMALL[name], out_dtype="bf16")
     rows = H.all_rows(r)
     H.attn_rows_crossfed(r, rows, "bf16-out")
+
+
+# The pages' other forms of the two rules: the additive metric
+# s + beta*max(0, log w^2), routing alone (w ignored), and the linear budget
+# from k_start to mu*k_start.
+MODES = {
+    "bf16-b64-d128-additive": syn.custom([1000, 77, 0, 2050], 8, 2, 128, "bf16", 64,
+                                         sink_blocks=2, k_min=3, rho0=0.5, tau=8.0, seed=41,
+                                         metric="additive", beta=0.5),
+    "bf16-b128-d64-routing": syn.custom([1337, 1], 4, 2, 64, "bf16", 128, sink_blocks=1,
+                                        k_min=1, rho0=0.4, tau=3.0, seed=42, metric="routing"),
+    "bf16-b128-d128-linear": syn.custom([4100, 300], 4, 1, 128, "bf16", 128, sink_blocks=1,
+                                        k_min=2, seed=43, budget_mode="linear", k_start=12.0,
+                                        mu=0.25),
+    "f32-b64-d128-additive-linear": syn.custom([555, 900], 4, 2, 128, "f32", 64,
+                                               sink_blocks=1, k_min=1, seed=44,
+                                               budget_mode="linear", k_start=6.5, mu=0.5,
+                                               metric="additive", beta=1.5),
+    "f32-b128-d64-routing": syn.custom([640], 2, 1, 64, "f32", 128, rope_theta=None,
+                                       sink_blocks=0, k_min=1, rho0=0.5, tau=2.0, seed=45,
+                                       metric="routing"),
+}
+
+
+@pytest.mark.parametrize("name", list(MODES))
+def test_metric_and_budget_modes_every_stage(name):
+    _cuda()
+    H.log(f"case mode {name}")
+    _full_check(H.GpuRun(MODES[name]))
 
 
 def test_single_head_1k_fp32_workload():
@@ -154,8 +185,8 @@ def test_equal_scores_pick_smallest_blocks():
 # ----------------------------------------------------------------- full size
 
 
-def _full_size(name: str, n_attn_rows: int):
-    w = syn.WORKLOADS[name]
+def _full_size(name: str, n_attn_rows: int, **params):
+    w = syn.WORKLOADS[name].replace(**params)
     H.log(f"case full-size {name}: generating inputs")
     r = H.GpuRun(w, out_dtype="bf16")
     H.log(f"case full-size {name}: GPU done, checking pooled values")
@@ -169,6 +200,9 @@ def _full_size(name: str, n_attn_rows: int):
     H.log(f"case full-size {name}: selection rows (all)")
     H.select_rows_crossfed(r, H.all_rows(r))
     assert np.array_equal(r.count.sum(axis=1), np.full(w.num_q_heads, r.budget.sum()))
+    np.testing.assert_array_equal(
+        r.budget, O.budgets_for(r.cu_blocks, w.sink_blocks, w.k_min, w.rho0, w.tau,
+                                w.budget_mode, w.k_start, w.mu))
     H.log(f"case full-size {name}: metric rows (sampled)")
     qbar = O.pool_mean(r.x.q, w.cu_seqlens, w.block)
     kbar = O.pool_mean(r.x.k, w.cu_seqlens, w.block)
@@ -176,9 +210,10 @@ def _full_size(name: str, n_attn_rows: int):
     seq_of = np.repeat(np.arange(len(r.cu_blocks) - 1), np.diff(r.cu_blocks))
     for (h, b) in H.sample_rows(r, 256, seed=1):
         s = int(seq_of[b]); i = b - int(r.cu_blocks[s])
-        ref = O.score_row_values(qbar, kbar, wref, r.cu_blocks, w.head_dim, h, s, i)
+        ref = O.score_row_values(qbar, kbar, wref, r.cu_blocks, w.head_dim, h, s, i,
+                                 w.metric, w.beta)
         got = r.scores[h, int(offs[s]) + O.tri(i):][:i + 1]
-        H.check_scores(got, ref, w.dtype, f"scores {(h, b)}")
+        H.check_scores(got, ref, w.dtype, f"scores {(h, b)}", w.metric)
     H.log(f"case full-size {name}: attention rows (sampled)")
     worst, lw = H.attn_rows_crossfed(r, H.sample_rows(r, n_attn_rows, seed=2))
     H.log(f"case full-size {name}: attention max err {worst:.3g}, lse {lw:.3g}")
@@ -190,3 +225,11 @@ def _full_size(name: str, n_attn_rows: int):
 def test_full_size_workload(name):
     _cuda()
     _full_size(name, 96)
+
+
+@pytest.mark.timeout(900)
+def test_full_size_additive_metric_linear_budget():
+    """The 32K layer with the pages' additive metric and linear budget."""
+    _cuda()
+    _full_size("llama3-8b-32k-b64", 64, metric="additive", beta=0.5, budget_mode="linear",
+               k_start=24.0, mu=0.25)

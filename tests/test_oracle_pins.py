@@ -165,6 +165,60 @@ def test_metric_orders_like_additive_oam_with_half_beta():
                                   np.argsort(-additive, kind="stable"))
 
 
+def test_additive_metric_hand_computed_row():
+    # d = 4 (scale 1/2), qbar_2 = 2 e1, kbar = [0, e1, -e1] -> s = [0, 1, -1];
+    # w = [e, 1/2, 0]: log w^2 = [2, -2 ln 2, -inf] -> bonus beta*[2, 0, 0].
+    qbar = np.zeros((1, 3, 4)); qbar[0, 2, 0] = 2.0
+    kbar = np.zeros((1, 3, 4)); kbar[0, 1, 0] = 1.0; kbar[0, 2, 0] = -1.0
+    w = np.array([[math.e, 0.5, 0.0]])
+    m = O.score(qbar, kbar, w, np.array([0, 3]), 4, metric="additive", beta=0.75)
+    row = O.score_row(m, np.array([0, 3]), 0, 0, 2)
+    np.testing.assert_allclose(row, [0.75 * 2.0, 1.0, -1.0], rtol=1e-15, atol=1e-15)
+    # beta = 0 leaves the scaled logits alone
+    m0 = O.score(qbar, kbar, w, np.array([0, 3]), 4, metric="additive", beta=0.0)
+    np.testing.assert_allclose(O.score_row(m0, np.array([0, 3]), 0, 0, 2), [0.0, 1.0, -1.0],
+                               atol=1e-15)
+
+
+def test_additive_metric_rows_are_not_normalised():
+    # the additive form has no softmax: adding a constant to every logit of a
+    # row (a query component along a direction all kbar share) shifts the row
+    r = rng(71)
+    nb, d = 6, 8
+    kbar = r.standard_normal((1, nb, d)); kbar[0, :, 0] = 1.0
+    qbar = r.standard_normal((1, nb, d)); qbar[0, :, 0] = 0.0
+    q2 = qbar.copy(); q2[0, :, 0] = 3.0
+    w = r.uniform(0.5, 4.0, (1, nb))
+    cub = np.array([0, nb])
+    a = O.score(qbar, kbar, w, cub, d, metric="additive", beta=0.3)
+    b = O.score(q2, kbar, w, cub, d, metric="additive", beta=0.3)
+    np.testing.assert_allclose(b - a, 3.0 / math.sqrt(d), rtol=1e-12)
+
+
+def test_routing_metric_is_softmax_and_ignores_w():
+    r = rng(72)
+    nb, d = 9, 16
+    qbar = r.standard_normal((2, nb, d))
+    kbar = r.standard_normal((1, nb, d))
+    w = r.uniform(0.1, 9.0, (1, nb))
+    cub = np.array([0, nb])
+    m = O.score(qbar, kbar, w, cub, d, metric="routing")
+    for h in range(2):
+        for i in range(nb):
+            lg = kbar[0, :i + 1] @ qbar[h, i] / 4.0
+            np.testing.assert_allclose(O.score_row(m, cub, h, 0, i),
+                                       scipy.special.softmax(lg), rtol=1e-13)
+    # and equals the output-aware metric with every w = 1
+    m1 = O.score(qbar, kbar, np.ones_like(w), cub, d)
+    np.testing.assert_allclose(m, m1, rtol=1e-15)
+
+
+def test_unknown_metric_is_rejected():
+    with pytest.raises(ValueError):
+        O.score(np.zeros((1, 1, 4)), np.zeros((1, 1, 4)), np.ones((1, 1)), np.array([0, 1]), 4,
+                metric="oam")
+
+
 # ---------------------------------------------------------------- budget
 
 
@@ -209,10 +263,31 @@ def test_budget_closed_forms():
 
 
 def test_budget_linear_endpoints():
-    b = O.budget_linear(101, 2, 20, 0.7)
+    b = O.budget_linear(101, 2, 0, 20, 0.7)
     assert b[2] == 3                               # row 2 has only 3 causal blocks
     assert b[50] == 2 + 1 + math.ceil(20 * 0.5 + 14 * 0.5)
     assert b[100] == 2 + 1 + 14                    # k_end = mu * k_start
+    # once the causal cap stops binding the dynamic part never rises
+    kd = b[25:] - 3
+    assert (np.diff(kd) <= 0).all() and kd[0] <= 20 and kd[-1] == 14
+
+
+def test_budget_linear_special_cases():
+    # mu = 1: uniform k_start (rounded up); k_min floors it
+    b = O.budget_linear(64, 1, 0, 5.5, 1.0)
+    assert list(b) == [1] + [min(i + 1, 1 + 1 + 6) for i in range(1, 64)]
+    b = O.budget_linear(64, 1, 9, 5.5, 1.0)
+    assert list(b) == [1] + [min(i + 1, 1 + 1 + 9) for i in range(1, 64)]
+    # mu = 0 decays to nothing but the floor at the last block
+    b = O.budget_linear(33, 0, 2, 16, 0.0)
+    assert b[32] == 1 + 2 and b[16] == 1 + 8
+    # one block: f = 0
+    assert list(O.budget_linear(1, 0, 0, 3, 0.5)) == [1]
+    # the per-sequence table restarts at every sequence
+    cub = np.array([0, 10, 10, 40])
+    t = O.budgets_for(cub, 2, 1, 0.0, 1.0, mode="linear", k_start=8, mu=0.25)
+    np.testing.assert_array_equal(t, np.concatenate([O.budget_linear(10, 2, 1, 8, 0.25),
+                                                     O.budget_linear(30, 2, 1, 8, 0.25)]))
 
 
 # ---------------------------------------------------------------- selection
