@@ -1,6 +1,7 @@
 """Benchmark of the Stem sparse-prefill path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+    python bench.py --sweep        latency against context length, Stem vs dense
 
 A step is one pass of the whole path over one batch of synthetic input with
 the inputs already resident in HBM: stem_pool -> stem_score -> stem_select
@@ -171,6 +172,54 @@ def copy_calibration(nbytes: int = 1 << 30):
     log(f"copy calibration: {nbytes} bytes read and written")
 
 
+SWEEP_TOKENS = (8192, 16384, 32768, 65536, 131072)
+
+
+def sweep(base_name: str, steps: int, warmup: int, dense_reps: int):
+    """Latency of the whole path and of the dense comparator (the same
+    attention kernel with every causal block kept) at growing context length,
+    with the head shape and Stem parameters of ``base_name``.  One JSON line
+    per length, then a summary line."""
+    import torch
+    from block_sparse_causal_amd import stem
+    from block_sparse_causal_amd import synthetic as syn
+    base = syn.WORKLOADS[base_name]
+    rows = []
+    for n, tokens in enumerate(SWEEP_TOKENS):
+        w = base.replace(name=f"{base_name}@{tokens // 1024}k", seqlens=(tokens,),
+                         seed=base.seed + 100 + n)
+        log(f"sweep {w.name}: generating inputs")
+        x = syn.generate(w)
+        q, k, v = upload(x)
+        del x
+        plan = stem.plan_for(w).to("cuda")
+        bufs = stem.Buffers(plan, "cuda", out_dtype=torch.bfloat16)
+        _, stage, total = time_path(plan, q, k, v, bufs, steps, warmup)
+        del bufs
+        step_ms = float(np.mean(total))
+        attn_ms = float(np.mean(stage[3]))
+        flops = attn_flops(plan, diag_half=True)
+        dms, dflops = dense_attention_ms(w, q, k, v, dense_reps)
+        row = {"tokens": tokens, "nb": int(plan.info.total_blocks),
+               "executed_blocks_per_head": int(plan.info.executed_blocks_per_head),
+               "stem_step_ms": round(step_ms, 4),
+               "stages_ms": {nm: round(float(np.mean(st_)), 4)
+                             for nm, st_ in zip(["pool", "score", "select", "attn"], stage)},
+               "stem_attn_tflops": round(flops / (attn_ms * 1e-3) / 1e12, 1),
+               "dense_attn_ms": round(dms, 3),
+               "dense_attn_tflops": round(dflops / (dms * 1e-3) / 1e12, 1),
+               "speedup": round(dms / step_ms, 2)}
+        log(f"sweep {tokens:>6} tokens: stem {step_ms:.3f} ms, dense {dms:.3f} ms, "
+            f"speed-up {dms / step_ms:.2f}x")
+        print(json.dumps({"sweep": base_name, **row}), flush=True)
+        rows.append(row)
+        del q, k, v, plan
+        torch.cuda.empty_cache()
+    print(json.dumps({"sweep": base_name, "summary": [
+        (r["tokens"], r["stem_step_ms"], r["dense_attn_ms"], r["speedup"]) for r in rows]}),
+        flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -181,6 +230,8 @@ def main():
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--sweep", action="store_true",
+                    help="latency against context length (8K..128K), Stem vs dense")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -193,6 +244,9 @@ def main():
     from block_sparse_causal_amd import synthetic as syn
 
     name = args.workload or syn.HEADLINE
+    if args.sweep:
+        sweep(name, args.steps, args.warmup, args.dense_reps)
+        return
     w = syn.WORKLOADS[name]
     log(f"workload {name}: generating seeded inputs")
     t = time.perf_counter()

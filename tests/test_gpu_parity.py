@@ -229,7 +229,8 @@ def test_full_size_workload(name):
 
 @pytest.mark.timeout(900)
 def test_full_size_additive_metric_linear_budget():
-    """The 32K layer with the pages' additive metric and linear budget."""
+    """The 32K layer with the pages' additive metric and linear budget, at the
+    ablation's best values beta = 0.2 and mu = 0.7."""
     _cuda()
-    _full_size("llama3-8b-32k-b64", 64, metric="additive", beta=0.5, budget_mode="linear",
-               k_start=24.0, mu=0.25)
+    _full_size("llama3-8b-32k-b64", 64, metric="additive", beta=0.2, budget_mode="linear",
+               k_start=24.0, mu=0.7)
