@@ -34,7 +34,7 @@ namespace stem {
 namespace {
 
 constexpr int kXcds = 8;
-constexpr float kRescaleLog2 = 8.0f;  // lazy-rescale threshold, log2 units
+constexpr float kRescaleBound = 256.f;  // lazy rescale: largest per-lane chunk weight sum (2^8)
 
 struct AttnArgs {
   const void *q, *k, *v;
@@ -233,8 +233,10 @@ void attn_bf16_kernel(AttnArgs a) {
   const int vd = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
   const int vsub = ((vd & 7) >> 2) * 8;
 
-  // One stage held in buffer `buf`, first key at local position key0: S
-  // for KT tiles of 32 keys, (mask), softmax, PV.
+  // One stage held in buffer `buf`, first key at local position key0.  The
+  // S tiles of every 32-key chunk of the stage are issued first, so that the
+  // matrix cores work on chunk u+1 while the vector unit runs the softmax of
+  // chunk u, and the PV products of chunk u overlap the softmax of chunk u+1.
   auto step = [&](auto mask_tag, int buf, int key0) {
     constexpr bool MASK = decltype(mask_tag)::value;
     if constexpr (MASK) {
@@ -244,59 +246,36 @@ void attn_bf16_kernel(AttnArgs a) {
     }
     const char *Kb = lds + buf * TILEB;
     const char *Vb = lds + (2 + buf) * TILEB;
+    // S^T = K Q^T for keys key0 + 32u .. +31
+    f32x16 sacc[KT];
 #pragma unroll
     for (int u = 0; u < KT; ++u) {
-      // S^T = K Q^T for keys key0 + 32u .. +31
-      f32x16 sacc = f32x16{};
+      sacc[u] = f32x16{};
       const int kr = u * 32 + n;
       const char *krow = Kb + kr * ROWB;
       const int ksw = swz_k(kr, NCH);
 #pragma unroll
       for (int c = 0; c < DC; ++c) {
         const u32x4 kx = *reinterpret_cast<const u32x4 *>(krow + (((2 * c + hi) ^ ksw) * 16));
-        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kx), qf[c], sacc,
-                                                      0, 0, 0);
+        sacc[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kx), qf[c],
+                                                         sacc[u], 0, 0, 0);
       }
+    }
+#pragma unroll
+    for (int u = 0; u < KT; ++u) {
       if constexpr (MASK) {
         // key position <= query position, and inside the sequence
         const int lim = min(qloc, r.seq_len - 1) - (key0 + u * 32 + 4 * hi);
 #pragma unroll
         for (int q = 0; q < 16; ++q)
-          if (8 * (q >> 2) + (q & 3) > lim) sacc[q] = -INFINITY;
+          if (8 * (q >> 2) + (q & 3) > lim) sacc[u][q] = -INFINITY;
       }
-      // online softmax; the reference maximum moves only when a row's
-      // maximum exceeds it by more than 2^8 in the exp2 domain, so most
-      // tiles skip rescaling the accumulators
-      float bm = -INFINITY;
-#pragma unroll
-      for (int q = 0; q < 16; ++q) bm = fmaxf(bm, sacc[q]);
-      bm = fmaxf(bm, __shfl_xor(bm, 32));
-      if (__ballot((bm - mrun) * cl2 > kRescaleLog2)) {
-        const float mnew = fmaxf(mrun, bm);
-        const float alpha = mnew == mrun ? 1.f : __builtin_amdgcn_exp2f((mrun - mnew) * cl2);
-        lrun *= alpha;
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) oacc[dt] *= alpha;
-        mrun = mnew;
-      }
-      // rows with every key so far masked keep mrun = -inf and p = 0
-      const float msc = mrun == -INFINITY ? 0.f : mrun * cl2;
-      float ps = 0.f;
-#pragma unroll
-      for (int q = 0; q < 16; ++q) {
-        const float p = __builtin_amdgcn_exp2f(fmaf(sacc[q], cl2, -msc));
-        sacc[q] = p;
-        ps += p;
-      }
-      lrun += ps;
-      // O^T += V^T P^T.  Contraction step hc covers keys kb0 + 4hi + {0..3}
-      // and kb0 + 8 + 4hi + {0..3} with kb0 = 32u + 16hc (stage rows);
-      // ds_read_b64_tr_b16 gives lane (n, hi) V[kb0 + 4hi + e][dt*32 + n].
+      // V^T fragments of this chunk (contraction step hc covers keys
+      // kb0 + 4hi + {0..3} and kb0 + 8 + 4hi + {0..3}, kb0 = 32u + 16hc;
+      // ds_read_b64_tr_b16 gives lane (n, hi) V[kb0 + 4hi + e][dt*32 + n])
+      bf16x8 vf[2][DT];
 #pragma unroll
       for (int hc = 0; hc < 2; ++hc) {
-        const f32x8 pv = {sacc[8 * hc + 0], sacc[8 * hc + 1], sacc[8 * hc + 2], sacc[8 * hc + 3],
-                          sacc[8 * hc + 4], sacc[8 * hc + 5], sacc[8 * hc + 6], sacc[8 * hc + 7]};
-        const bf16x8 pf = __builtin_convertvector(pv, bf16x8);
         const int r0 = u * 32 + 16 * hc + vrow;
         const char *p0 = Vb + r0 * ROWB + vsub;
         const char *p1 = p0 + 8 * ROWB;
@@ -306,11 +285,60 @@ void attn_bf16_kernel(AttnArgs a) {
           const int ch = (dt * 32 + vd) >> 3;
           const v4i16 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(p0 + ((ch ^ sw0) * 16)));
           const v4i16 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(p1 + ((ch ^ sw1) * 16)));
-          const bf16x8 vf = __builtin_bit_cast(bf16x8, (v8i16){v0[0], v0[1], v0[2], v0[3],
-                                                               v1[0], v1[1], v1[2], v1[3]});
-          oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf, oacc[dt], 0, 0, 0);
+          vf[hc][dt] = __builtin_bit_cast(bf16x8, (v8i16){v0[0], v0[1], v0[2], v0[3],
+                                                          v1[0], v1[1], v1[2], v1[3]});
         }
       }
+      // Online softmax against a lazily moved reference maximum mrun: the
+      // weights are exp2((s - mrun) * c); the reference is raised only when
+      // some weight of the chunk would exceed 2^8 (their per-lane sum is then
+      // above 2^8 as well).  A row that has seen no key yet has mrun = -inf,
+      // which makes its weights +inf or NaN and sends it down the same rare
+      // path.  The row sum is taken over the bf16-rounded weights, the ones
+      // that multiply V.
+      bf16x8 pf[2];
+      float ps;
+      auto weights = [&](float msc) {
+#pragma unroll
+        for (int hc = 0; hc < 2; ++hc) {
+          f32x8 pv;
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            pv[e] = __builtin_amdgcn_exp2f(fmaf(sacc[u][8 * hc + e], cl2, -msc));
+          pf[hc] = __builtin_convertvector(pv, bf16x8);
+        }
+        const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+        float sum = 0.f;
+#pragma unroll
+        for (int hc = 0; hc < 2; ++hc)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            sum = __builtin_amdgcn_fdot2_f32_bf16(
+                bf16x2{pf[hc][2 * e], pf[hc][2 * e + 1]}, one, sum, false);
+        ps = sum;
+      };
+      weights(mrun * cl2);
+      if (__ballot(!(ps <= kRescaleBound))) {
+        float bm = -INFINITY;
+#pragma unroll
+        for (int q = 0; q < 16; ++q) bm = fmaxf(bm, sacc[u][q]);
+        bm = fmaxf(bm, __shfl_xor(bm, 32));
+        const float mnew = fmaxf(mrun, bm);
+        const float alpha = mnew == mrun ? 1.f : __builtin_amdgcn_exp2f((mrun - mnew) * cl2);
+        lrun *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) oacc[dt] *= alpha;
+        mrun = mnew;
+        // rows with every key so far masked keep mrun = -inf and weight 0
+        weights(mrun == -INFINITY ? INFINITY : mrun * cl2);
+      }
+      lrun += ps;
+      // O^T += V^T P^T
+#pragma unroll
+      for (int hc = 0; hc < 2; ++hc)
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+          oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[hc][dt], pf[hc], oacc[dt], 0, 0, 0);
     }
   };
 
