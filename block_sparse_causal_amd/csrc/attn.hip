@@ -134,10 +134,11 @@ __device__ __forceinline__ void dma16(const void *gbase, uint32_t voff, uint32_t
 // compiler's own wait-count bookkeeping sees it.
 __device__ __forceinline__ void wait_vm() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
-template <int B, int D, bool OUT_BF16>
-__global__ __launch_bounds__(B * 2) __attribute__((amdgpu_waves_per_eu(2, 2)))
+template <int B, int D, int QW, bool OUT_BF16>
+__global__ __launch_bounds__(B / QW * 64) __attribute__((amdgpu_waves_per_eu(64 / QW, 64 / QW)))
 void attn_bf16_kernel(AttnArgs a) {
-  constexpr int NW = B / 32;           // wavefronts, 32 queries each
+  constexpr int QT = QW / 32;          // 32-query tiles per wavefront
+  constexpr int NW = B / QW;           // wavefronts
   constexpr int NT = NW * 64;          // threads
   constexpr int SK = B / 2;            // keys per stage
   constexpr int KT = SK / 32;          // 32-key MFMA tiles per stage
@@ -162,25 +163,33 @@ void attn_bf16_kernel(AttnArgs a) {
   const int Hq = a.Hq, Hkv = a.Hkv;
   const uint32_t lds_base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void *)lds));
 
-  // Q fragment of this wavefront's 32 queries (B operand of S^T = K Q^T)
-  const int qloc = r.i * B + w * 32 + n;
-  const bool qvalid = qloc < r.seq_len;
-  bf16x8 qf[DC];
-  {
+  // Q fragments of this wavefront's QW queries (B operand of S^T = K Q^T):
+  // tile qt holds queries w*QW + 32qt + n
+  int qloc[QT];
+  bf16x8 qf[QT][DC];
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) {
+    qloc[qt] = r.i * B + w * QW + qt * 32 + n;
+    const bool qvalid = qloc[qt] < r.seq_len;
     const uint16_t *qp = static_cast<const uint16_t *>(a.q) +
-                         ((r.seq_start + (qvalid ? qloc : 0)) * Hq + r.h) * int64_t(D) + hi * 8;
+                         ((r.seq_start + (qvalid ? qloc[qt] : 0)) * Hq + r.h) * int64_t(D) + hi * 8;
 #pragma unroll
     for (int c = 0; c < DC; ++c) {
       u32x4 x = qvalid ? *reinterpret_cast<const u32x4 *>(qp + c * 16) : u32x4{0u, 0u, 0u, 0u};
-      qf[c] = __builtin_bit_cast(bf16x8, x);
+      qf[qt][c] = __builtin_bit_cast(bf16x8, x);
     }
   }
   wait_vm();  // Q resident before the loop: no wait on it inside
 
-  f32x16 oacc[DT];
+  f32x16 oacc[QT][DT];
+  float mrun[QT], lrun[QT];
 #pragma unroll
-  for (int dt = 0; dt < DT; ++dt) oacc[dt] = f32x16{};
-  float mrun = -INFINITY, lrun = 0.f;
+  for (int qt = 0; qt < QT; ++qt) {
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) oacc[qt][dt] = f32x16{};
+    mrun[qt] = -INFINITY;
+    lrun[qt] = 0.f;
+  }
   const float cl2 = a.scale_log2;
 
   // Stage keys [key0, key0 + SK) of block j into buffer `buf` (asynchronous).
@@ -237,38 +246,46 @@ void attn_bf16_kernel(AttnArgs a) {
   // S tiles of every 32-key chunk of the stage are issued first, so that the
   // matrix cores work on chunk u+1 while the vector unit runs the softmax of
   // chunk u, and the PV products of chunk u overlap the softmax of chunk u+1.
-  auto step = [&](auto mask_tag, int buf, int key0) {
+  // Every K and V^T operand read from LDS feeds QT matrix products.
+  auto step = [&](auto mask_tag, int buf, int key0, auto &&after_s) {
     constexpr bool MASK = decltype(mask_tag)::value;
     if constexpr (MASK) {
       // nothing visible to this wavefront in this stage (future keys or
       // past the end of the sequence): skip it (wave-uniform)
-      if (key0 > r.i * B + w * 32 + 31 || key0 >= r.seq_len) return;
+      if (key0 > r.i * B + w * QW + QW - 1 || key0 >= r.seq_len) return;
     }
     const char *Kb = lds + buf * TILEB;
     const char *Vb = lds + (2 + buf) * TILEB;
     // S^T = K Q^T for keys key0 + 32u .. +31
-    f32x16 sacc[KT];
+    f32x16 sacc[KT][QT];
 #pragma unroll
     for (int u = 0; u < KT; ++u) {
-      sacc[u] = f32x16{};
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt) sacc[u][qt] = f32x16{};
       const int kr = u * 32 + n;
       const char *krow = Kb + kr * ROWB;
       const int ksw = swz_k(kr, NCH);
 #pragma unroll
       for (int c = 0; c < DC; ++c) {
-        const u32x4 kx = *reinterpret_cast<const u32x4 *>(krow + (((2 * c + hi) ^ ksw) * 16));
-        sacc[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kx), qf[c],
-                                                         sacc[u], 0, 0, 0);
+        const bf16x8 kx = __builtin_bit_cast(
+            bf16x8, *reinterpret_cast<const u32x4 *>(krow + (((2 * c + hi) ^ ksw) * 16)));
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt)
+          sacc[u][qt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kx, qf[qt][c], sacc[u][qt], 0, 0, 0);
       }
     }
+    after_s();  // the next stage's DMA goes out while the matrix cores work
 #pragma unroll
     for (int u = 0; u < KT; ++u) {
       if constexpr (MASK) {
         // key position <= query position, and inside the sequence
-        const int lim = min(qloc, r.seq_len - 1) - (key0 + u * 32 + 4 * hi);
 #pragma unroll
-        for (int q = 0; q < 16; ++q)
-          if (8 * (q >> 2) + (q & 3) > lim) sacc[u][q] = -INFINITY;
+        for (int qt = 0; qt < QT; ++qt) {
+          const int lim = min(qloc[qt], r.seq_len - 1) - (key0 + u * 32 + 4 * hi);
+#pragma unroll
+          for (int q = 0; q < 16; ++q)
+            if (8 * (q >> 2) + (q & 3) > lim) sacc[u][qt][q] = -INFINITY;
+        }
       }
       // V^T fragments of this chunk (contraction step hc covers keys
       // kb0 + 4hi + {0..3} and kb0 + 8 + 4hi + {0..3}, kb0 = 32u + 16hc;
@@ -296,49 +313,56 @@ void attn_bf16_kernel(AttnArgs a) {
       // which makes its weights +inf or NaN and sends it down the same rare
       // path.  The row sum is taken over the bf16-rounded weights, the ones
       // that multiply V.
-      bf16x8 pf[2];
-      float ps;
-      auto weights = [&](float msc) {
+      bf16x8 pf[QT][2];
 #pragma unroll
-        for (int hc = 0; hc < 2; ++hc) {
-          f32x8 pv;
+      for (int qt = 0; qt < QT; ++qt) {
+        float ps;
+        auto weights = [&](float msc) {
 #pragma unroll
-          for (int e = 0; e < 8; ++e)
-            pv[e] = __builtin_amdgcn_exp2f(fmaf(sacc[u][8 * hc + e], cl2, -msc));
-          pf[hc] = __builtin_convertvector(pv, bf16x8);
+          for (int hc = 0; hc < 2; ++hc) {
+            f32x8 pv;
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+              pv[e] = __builtin_amdgcn_exp2f(fmaf(sacc[u][qt][8 * hc + e], cl2, -msc));
+            pf[qt][hc] = __builtin_convertvector(pv, bf16x8);
+          }
+          const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+          float sum = 0.f;
+#pragma unroll
+          for (int hc = 0; hc < 2; ++hc)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              sum = __builtin_amdgcn_fdot2_f32_bf16(
+                  bf16x2{pf[qt][hc][2 * e], pf[qt][hc][2 * e + 1]}, one, sum, false);
+          ps = sum;
+        };
+        weights(mrun[qt] * cl2);
+        if (__ballot(!(ps <= kRescaleBound))) {
+          float bm = -INFINITY;
+#pragma unroll
+          for (int q = 0; q < 16; ++q) bm = fmaxf(bm, sacc[u][qt][q]);
+          bm = fmaxf(bm, __shfl_xor(bm, 32));
+          const float mnew = fmaxf(mrun[qt], bm);
+          const float alpha =
+              mnew == mrun[qt] ? 1.f : __builtin_amdgcn_exp2f((mrun[qt] - mnew) * cl2);
+          lrun[qt] *= alpha;
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt) oacc[qt][dt] *= alpha;
+          mrun[qt] = mnew;
+          // rows with every key so far masked keep mrun = -inf and weight 0
+          weights(mnew == -INFINITY ? INFINITY : mnew * cl2);
         }
-        const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
-        float sum = 0.f;
-#pragma unroll
-        for (int hc = 0; hc < 2; ++hc)
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            sum = __builtin_amdgcn_fdot2_f32_bf16(
-                bf16x2{pf[hc][2 * e], pf[hc][2 * e + 1]}, one, sum, false);
-        ps = sum;
-      };
-      weights(mrun * cl2);
-      if (__ballot(!(ps <= kRescaleBound))) {
-        float bm = -INFINITY;
-#pragma unroll
-        for (int q = 0; q < 16; ++q) bm = fmaxf(bm, sacc[u][q]);
-        bm = fmaxf(bm, __shfl_xor(bm, 32));
-        const float mnew = fmaxf(mrun, bm);
-        const float alpha = mnew == mrun ? 1.f : __builtin_amdgcn_exp2f((mrun - mnew) * cl2);
-        lrun *= alpha;
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) oacc[dt] *= alpha;
-        mrun = mnew;
-        // rows with every key so far masked keep mrun = -inf and weight 0
-        weights(mrun == -INFINITY ? INFINITY : mrun * cl2);
+        lrun[qt] += ps;
       }
-      lrun += ps;
       // O^T += V^T P^T
 #pragma unroll
       for (int hc = 0; hc < 2; ++hc)
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt)
-          oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[hc][dt], pf[hc], oacc[dt], 0, 0, 0);
+#pragma unroll
+          for (int qt = 0; qt < QT; ++qt)
+            oacc[qt][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[hc][dt], pf[qt][hc],
+                                                                   oacc[qt][dt], 0, 0, 0);
     }
   };
 
@@ -364,45 +388,49 @@ void attn_bf16_kernel(AttnArgs a) {
     for (int t = 0; t + 1 < nkeep; ++t) {
       wait_vm();
       __syncthreads();
-      issue(jcur, 1, 1);                      // second half of this block
-      step(std::false_type{}, 0, jcur * B);
+      // second half of this block
+      step(std::false_type{}, 0, jcur * B, [&] { issue(jcur, 1, 1); });
       const int jn = entry(t + 1);
       wait_vm();
       __syncthreads();
-      issue(jn, 0, 0);                        // first half of the next block
-      step(std::false_type{}, 1, jcur * B + SK);
+      // first half of the next block
+      step(std::false_type{}, 1, jcur * B + SK, [&] { issue(jn, 0, 0); });
       jcur = jn;
     }
     wait_vm();
     __syncthreads();
     issue(jcur, 1, 1);
-    step(std::true_type{}, 0, jcur * B);
+    step(std::true_type{}, 0, jcur * B, [] {});
     wait_vm();
     __syncthreads();
-    step(std::true_type{}, 1, jcur * B + SK);
+    step(std::true_type{}, 1, jcur * B + SK, [] {});
   }
 
   // ---- finalize: O^T lane layout = query n, dims dt*32 + 8(q/4) + 4hi + q%4
-  const float ltot = lrun + __shfl_xor(lrun, 32);
-  if (!qvalid) return;
-  const float inv = 1.0f / ltot;
-  const int64_t orow = ((r.seq_start + qloc) * Hq + r.h) * int64_t(D);
 #pragma unroll
-  for (int dt = 0; dt < DT; ++dt)
+  for (int qt = 0; qt < QT; ++qt) {
+    const float ltot = lrun[qt] + __shfl_xor(lrun[qt], 32);
+    if (qloc[qt] >= r.seq_len) continue;
+    const float inv = 1.0f / ltot;
+    const int64_t orow = ((r.seq_start + qloc[qt]) * Hq + r.h) * int64_t(D);
 #pragma unroll
-    for (int rg = 0; rg < 4; ++rg) {
-      const int d0 = dt * 32 + 8 * rg + 4 * hi;
-      const float o0 = oacc[dt][4 * rg] * inv, o1 = oacc[dt][4 * rg + 1] * inv;
-      const float o2 = oacc[dt][4 * rg + 2] * inv, o3 = oacc[dt][4 * rg + 3] * inv;
-      if (OUT_BF16) {
-        uint32_t *op = reinterpret_cast<uint32_t *>(static_cast<uint16_t *>(a.out) + orow + d0);
-        op[0] = pack_bf16x2(o0, o1);
-        op[1] = pack_bf16x2(o2, o3);
-      } else {
-        *reinterpret_cast<f32x4 *>(static_cast<float *>(a.out) + orow + d0) = f32x4{o0, o1, o2, o3};
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int rg = 0; rg < 4; ++rg) {
+        const int d0 = dt * 32 + 8 * rg + 4 * hi;
+        const float o0 = oacc[qt][dt][4 * rg] * inv, o1 = oacc[qt][dt][4 * rg + 1] * inv;
+        const float o2 = oacc[qt][dt][4 * rg + 2] * inv, o3 = oacc[qt][dt][4 * rg + 3] * inv;
+        if (OUT_BF16) {
+          uint32_t *op = reinterpret_cast<uint32_t *>(static_cast<uint16_t *>(a.out) + orow + d0);
+          op[0] = pack_bf16x2(o0, o1);
+          op[1] = pack_bf16x2(o2, o3);
+        } else {
+          *reinterpret_cast<f32x4 *>(static_cast<float *>(a.out) + orow + d0) = f32x4{o0, o1, o2, o3};
+        }
       }
-    }
-  if (a.lse && hi == 0) a.lse[int64_t(r.h) * a.T + r.seq_start + qloc] = mrun * a.scale + logf(ltot);
+    if (a.lse && hi == 0)
+      a.lse[int64_t(r.h) * a.T + r.seq_start + qloc[qt]] = mrun[qt] * a.scale + logf(ltot);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -549,10 +577,13 @@ __global__ __launch_bounds__(B * 2) void attn_f32_kernel(AttnArgs a) {
 template <template <int, int, bool> class K>
 struct Dummy;
 
+// queries per wavefront of the bf16 kernel
+constexpr int kQW = 32;
+
 template <bool BF16IN, int B, int D, bool OB>
 hipError_t launch_one(const AttnArgs &a, dim3 grid, hipStream_t st) {
   if (BF16IN)
-    hipLaunchKernelGGL((attn_bf16_kernel<B, D, OB>), grid, dim3(B * 2), 0, st, a);
+    hipLaunchKernelGGL((attn_bf16_kernel<B, D, kQW, OB>), grid, dim3(B / kQW * 64), 0, st, a);
   else
     hipLaunchKernelGGL((attn_f32_kernel<B, D, OB>), grid, dim3(B * 2), 0, st, a);
   return hipGetLastError();
