@@ -107,32 +107,6 @@ __device__ __forceinline__ int swz_v(int row, int nch) {
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef short v8i16 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
-typedef __attribute__((address_space(3))) void lds_void;
-
-// One wavefront-wide 16-byte-per-lane DMA from global memory into LDS:
-// lane l's 16 bytes land at LDS byte address lds_addr + 16 l.  Issued from
-// inline assembly so that the compiler does not track the LDS write: it
-// would otherwise wait for the in-flight prefetch of the next stage before
-// every read of the current one.  The kernel orders the DMA explicitly
-// (s_waitcnt vmcnt(0) + barrier before a stage is read).  The global
-// address is a wave-uniform base (SGPRs) plus a 32-bit per-lane byte
-// offset; M0, which carries the LDS address, is saved and restored.
-__device__ __forceinline__ void dma16(const void *gbase, uint32_t voff, uint32_t lds_addr) {
-  uint32_t saved;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %3\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %1, %2\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "v"(voff), "s"(gbase), "s"(lds_addr)
-      : "memory");
-}
-
-// s_waitcnt vmcnt(0) (expcnt and lgkmcnt untouched), as a builtin so that the
-// compiler's own wait-count bookkeeping sees it.
-__device__ __forceinline__ void wait_vm() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 template <int B, int D, int QW, bool OUT_BF16>
 __global__ __launch_bounds__(B / QW * 64) __attribute__((amdgpu_waves_per_eu(64 / QW, 64 / QW)))
@@ -161,7 +135,7 @@ void attn_bf16_kernel(AttnArgs a) {
   const int n = lane & 31;
   const int hi = lane >> 5;
   const int Hq = a.Hq, Hkv = a.Hkv;
-  const uint32_t lds_base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void *)lds));
+  const uint32_t lds_base = lds_addr_of(lds);
 
   // Q fragments of this wavefront's QW queries (B operand of S^T = K Q^T):
   // tile qt holds queries w*QW + 32qt + n

@@ -3,17 +3,21 @@
 // initial blocks are always kept because every later token aggregates them,
 // gist.science/es section 1 and gist.science/fr section 1).
 //
-// One 64-wide wavefront per (query head, query block) row.  The row's
-// candidate metrics are read once (coalesced) into registers as
-// order-preserving 32-bit keys.  The k-th largest key is found by a bitwise
-// bisection (from the highest bit in which the row's largest and smallest
-// keys differ) whose counts come from wavefront ballots (v_cmp straight into
-// a scalar mask, popcount on the scalar unit), so the cost does not depend
-// on k.  Keys above the threshold are kept; keys equal to it are kept
-// in ascending block order until the budget is met, which is exactly "larger
-// metric first, equal metrics to the smaller block number".  The kept blocks
-// are written in ascending order with ballot/mbcnt compaction, after the
-// forced sink blocks and before the forced diagonal block.
+// One 64-wide wavefront per (query head, query block) row, rows dispatched
+// longest first.  The row's candidate metrics are read once (coalesced) into
+// registers as order-preserving 32-bit keys.  Thresholds are found by a
+// bitwise bisection (from the highest bit in which the largest and smallest
+// key differ) whose counts come from wavefront ballots (v_cmp straight into
+// a scalar mask, popcount on the scalar unit).  Fast path (budget <= 64):
+// the take-th largest of the 64 per-lane maxima bounds the threshold from
+// below; the few keys that reach it are compacted, in block order, into one
+// register per lane and the exact threshold is found there with one ballot
+// per bit.  Otherwise the bisection runs over every key.  Keys above the
+// threshold are kept; keys equal to it are kept in ascending block order
+// until the budget is met, which is exactly "larger metric first, equal
+// metrics to the smaller block number".  The kept blocks are written in
+// ascending order with ballot/mbcnt compaction, after the forced sink
+// blocks and before the forced diagonal block.
 #include "stem_device.h"
 #include "stem_internal.h"
 
@@ -42,11 +46,31 @@ __device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
                                    __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(mask), 0u));
 }
 
+// Largest T with #{lanes l: v_l >= T} >= need (need >= 1 lanes hold v >= lo,
+// every v that counts is >= lo >= 1 and <= hi): bitwise bisection from the
+// highest bit in which lo and hi differ.
+__device__ __forceinline__ uint32_t kth_largest(uint32_t v, uint32_t lo, uint32_t hi, int need) {
+  const uint32_t diff = lo ^ hi;
+  const int top = diff ? 31 - __builtin_clz(diff) : -1;
+  uint32_t T = top < 0 ? hi : (top >= 31 ? 0u : (hi & ~((2u << top) - 1u)));
+  for (int bit = top; bit >= 0; --bit) {
+    const uint32_t cand = T | (1u << bit);
+    if (__popcll(__ballot(v >= cand)) >= need) T = cand;
+  }
+  return T;
+}
+
 template <int E>
 __global__ __launch_bounds__(256) void select_kernel(SelectArgs a) {
+  // per wavefront: the few candidates that can still reach the top
+  __shared__ uint32_t ckey[4][64];
+  __shared__ int32_t cpos[4][64];
   const int lane = threadIdx.x & 63;
-  const int64_t row = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
-  if (row >= int64_t(a.Hq) * a.nbT) return;
+  const int wv = threadIdx.x >> 6;
+  // rows in reverse order: the longest rows (last query blocks) go first
+  const int64_t nrows = int64_t(a.Hq) * a.nbT;
+  const int64_t row = nrows - 1 - (int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6));
+  if (row < 0) return;
   const int h = static_cast<int>(row / a.nbT);
   const int b = static_cast<int>(row % a.nbT);
   const int s = a.pd.blk_seq[b];
@@ -82,6 +106,53 @@ __global__ __launch_bounds__(256) void select_kernel(SelectArgs a) {
     kmn = c ? min(kmn, key[e]) : kmn;
   }
   const int ne = (ncand + 63) >> 6;  // chunks holding candidates (wave-uniform)
+  // Fast path.  L = the take-th largest of the 64 per-lane maxima is a lower
+  // bound of the take-th largest key (take lanes each hold a key >= L).  When
+  // at most 64 keys reach L they are compacted, in block order, into one
+  // register per lane and the exact threshold is found there.
+  if (take >= 1 && take <= 64) {
+    uint32_t lmax = 0u;
+#pragma unroll
+    for (int e = 0; e < E; ++e) lmax = max(lmax, key[e]);
+    uint32_t wmax = lmax, wmin = lmax ? lmax : 0xffffffffu;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+      wmax = max(wmax, static_cast<uint32_t>(__shfl_xor(static_cast<int>(wmax), o)));
+      wmin = min(wmin, static_cast<uint32_t>(__shfl_xor(static_cast<int>(wmin), o)));
+    }
+    const uint32_t L = kth_largest(lmax, wmin, wmax, take);
+    int nc = 0;
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+      if (e < ne) nc += __popcll(__ballot(key[e] >= L));
+    if (nc <= 64) {
+      int base = 0;
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        if (e >= ne) break;
+        const bool c = key[e] >= L;
+        const uint64_t m = __ballot(c);
+        if (c) {
+          const int p = base + static_cast<int>(lanes_below(m));
+          ckey[wv][p] = key[e];
+          cpos[wv][p] = S + lane + 64 * e;
+        }
+        base += __popcll(m);
+      }
+      const uint32_t ck = lane < nc ? ckey[wv][lane] : 0u;
+      const int cj = lane < nc ? cpos[wv][lane] : 0;
+      const uint32_t T = kth_largest(ck, L, wmax, take);
+      const int gt = __popcll(__ballot(ck > T));
+      const uint64_t eqm = __ballot(ck == T);
+      const bool sel = ck > T || (ck == T && static_cast<int>(lanes_below(eqm)) < take - gt);
+      const uint64_t sm = __ballot(sel);
+      if (sel) out[S + static_cast<int>(lanes_below(sm))] = cj;
+      for (int p = lane; p < S; p += 64) out[p] = p;
+      if (lane == 0) out[S + take] = i;
+      for (int p = S + take + 1 + lane; p < a.kmax; p += 64) out[p] = -1;
+      return;
+    }
+  }
   // largest T with #{key >= T} >= take (take >= 1 here, and all
   // candidates have key >= 1, so T >= 1 and padding never qualifies).
   // T lies between the row's smallest and largest key, so the bits above

@@ -56,6 +56,37 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
 }
 
+// One wavefront-wide 16-byte-per-lane DMA from global memory into LDS:
+// lane l's 16 bytes land at LDS byte address lds_addr + 16 l.  Issued from
+// inline assembly so that the compiler does not track the LDS write (it
+// would otherwise wait for an in-flight prefetch before every unrelated LDS
+// read); callers order it explicitly with s_waitcnt vmcnt (and a barrier
+// when other wavefronts read the data).  The global address is a
+// wave-uniform base (SGPRs) plus a 32-bit per-lane byte offset; M0, which
+// carries the LDS address, is saved and restored.
+__device__ __forceinline__ void dma16(const void *gbase, uint32_t voff, uint32_t lds_addr) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %2\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(voff), "s"(gbase), "s"(lds_addr)
+      : "memory");
+}
+
+// s_waitcnt vmcnt(0) / lgkmcnt(0) alone, as builtins so that the compiler's
+// own wait-count bookkeeping sees them.
+__device__ __forceinline__ void wait_vm() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+__device__ __forceinline__ void wait_lgkm() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
+// LDS byte address (what M0 and ds_* instructions take) of a __shared__ object.
+__device__ __forceinline__ uint32_t lds_addr_of(const void *p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const void *)p));
+}
+
 // Launchers (return hipSuccess or the launch error).
 hipError_t launch_pool(const stem_plan_info &in, PlanDev pd, const void *q,
                        const void *k, const void *v, float *qbar, float *kbar,

@@ -182,6 +182,29 @@ def test_equal_scores_pick_smallest_blocks():
     H.select_rows_crossfed(r, H.all_rows(r))
 
 
+def test_select_long_budget_and_wide_ties():
+    """Both selection strategies: budgets of more than 64 free slots (every
+    key takes part in the threshold search), and rows whose metrics are all
+    equal with more than 64 candidates tied at the threshold."""
+    _cuda()
+    w = syn.custom([64 * 300], 2, 1, 128, "bf16", 64, sink_blocks=2, k_min=100, rho0=0.0,
+                   tau=1.0, seed=51)
+    H.log("case select k_min=100")
+    _full_check(H.GpuRun(w))
+    w = syn.custom([64 * 200], 2, 1, 128, "bf16", 64, sink_blocks=2, k_min=5, rho0=0.0, tau=1.0)
+    x = syn.generate(w)
+    one = syn.bf16_bits(np.ones(1, np.float32))[0]
+    x.k_bits[:] = one; x.v_bits[:] = one
+    x.k[:] = 1.0; x.v[:] = 1.0
+    H.log("case select 200 tied blocks")
+    r = H.GpuRun(w, x=x)
+    for h in range(2):
+        for i in range(200):
+            want = list(range(i + 1)) if i < 8 else list(range(7)) + [i]
+            assert list(r.idx[h, i, :r.count[h, i]]) == want, (h, i)
+    H.select_rows_crossfed(r, H.all_rows(r))
+
+
 # ----------------------------------------------------------------- full size
 
 
