@@ -82,12 +82,14 @@ __device__ __forceinline__ bool decode_item(const AttnArgs &a, Row &r) {
 //
 // Workgroup = B/32 wavefronts for one (head, query block) row, wavefront w
 // owning queries 32w .. 32w+31.  Each kept key block is streamed through
-// LDS in two stages of B/2 keys; stages are double-buffered and filled by
-// direct global->LDS DMA (global_load_lds_dwordx4, no registers) one stage
-// ahead of the compute.  A workgroup then needs 4 B/2 d 2 bytes of LDS
-// (64 KiB at B = d = 128), so two workgroups share a CU: their barriers are
-// independent, and one's softmax, LDS reads and DMA waits overlap the
-// other's MFMAs on the same SIMDs.
+// LDS in stages of 32 keys, filled by direct global->LDS DMA
+// (global_load_lds_dwordx4, no registers) ahead of the compute.  At
+// B = 128 three stage buffers (48 KiB at d = 128) keep the DMA two stages
+// ahead, and with at most 168 VGPRs per wavefront three workgroups share a
+// CU (three wavefronts per SIMD): their barriers are independent, so one's
+// softmax, LDS reads and DMA waits overlap the others' MFMAs.  At B = 64
+// (two-wavefront workgroups) two buffers suffice and LDS bounds the
+// occupancy instead of registers.
 //
 // K and V stages are row-major with an XOR swizzle of the 16-byte chunks:
 // K operand reads (ds_read_b128 of one key row) and V operand reads
@@ -96,8 +98,9 @@ __device__ __forceinline__ bool decode_item(const AttnArgs &a, Row &r) {
 //
 // Selection lists are ascending and end with the diagonal block (the only
 // block that needs the token-level causal mask, and the only one that can
-// be a partial block): the unmasked step runs for every stage of the other
-// blocks, the masked step for the two stages of the last one.
+// be a partial block): the unmasked step runs for the stages of every other
+// block, and the masked step for a short tail holding the last block's
+// stages.
 
 __device__ __forceinline__ int swz_k(int row, int nch) { return (row / (16 / nch)) % nch; }
 __device__ __forceinline__ int swz_v(int row, int nch) {
@@ -108,13 +111,33 @@ typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef short v8i16 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 
+constexpr int kStageKeys = 32;   // keys per LDS stage
+
+// Stage buffers: 3 (DMA two stages ahead, 48 KiB at d = 128) for B = 128,
+// where three 4-wavefront workgroups then share a CU; 2 for B = 64, where
+// the 2-wavefront workgroups are limited by LDS rather than registers.
+template <int B>
+constexpr int stage_bufs() { return B == 128 ? 3 : 2; }
+
+// f(std::integral_constant<int, I>()) for I = FIRST .. LAST - 1
+template <int FIRST, int LAST, typename F>
+__device__ __forceinline__ void static_for(F &&f) {
+  if constexpr (FIRST < LAST) {
+    f(std::integral_constant<int, FIRST>{});
+    static_for<FIRST + 1, LAST>(f);
+  }
+}
+
 template <int B, int D, int QW, bool OUT_BF16>
-__global__ __launch_bounds__(B / QW * 64) __attribute__((amdgpu_waves_per_eu(64 / QW, 64 / QW)))
+__global__ __launch_bounds__(B / QW * 64)
+__attribute__((amdgpu_waves_per_eu(QW == 32 ? (B == 128 ? 3 : 2) : 1, QW == 32 ? (B == 128 ? 3 : 2) : 1)))
 void attn_bf16_kernel(AttnArgs a) {
   constexpr int QT = QW / 32;          // 32-query tiles per wavefront
   constexpr int NW = B / QW;           // wavefronts
   constexpr int NT = NW * 64;          // threads
-  constexpr int SK = B / 2;            // keys per stage
+  constexpr int SK = kStageKeys;       // keys per stage
+  constexpr int NBUF = stage_bufs<B>(); // stage buffers
+  constexpr int NPB = B / SK;          // stages per key block
   constexpr int KT = SK / 32;          // 32-key MFMA tiles per stage
   constexpr int DT = D / 32;           // 32-dim output tiles
   constexpr int DC = D / 16;           // 16-dim contraction chunks for S
@@ -124,8 +147,8 @@ void attn_bf16_kernel(AttnArgs a) {
   constexpr int LOADS = TILEB / 16 / NT;
   static_assert(LOADS * 16 * NT == TILEB, "a stage must split into 16-byte loads");
   static_assert(NT % NCH == 0, "a load step covers whole rows");
-  // [K buf 0][K buf 1][V buf 0][V buf 1]
-  __shared__ __attribute__((aligned(16))) char lds[4 * TILEB];
+  // [K buf 0..NBUF-1][V buf 0..NBUF-1]
+  __shared__ __attribute__((aligned(16))) char lds[2 * NBUF * TILEB];
 
   Row r;
   if (!decode_item(a, r)) return;
@@ -176,18 +199,23 @@ void attn_bf16_kernel(AttnArgs a) {
   const int row0 = tid / NCH;
   const int pc0 = tid % NCH;
   const uint32_t rowbytes = static_cast<uint32_t>(Hkv) * D * 2;   // between token rows
-  uint32_t koff[LOADS], voff[LOADS];
-#pragma unroll
-  for (int it = 0; it < LOADS; ++it) {
-    const int row = row0 + it * ROWSTEP;
-    koff[it] = row * rowbytes + (pc0 ^ swz_k(row, NCH)) * 16;
-    voff[it] = row * rowbytes + (pc0 ^ swz_v(row, NCH)) * 16;
-  }
+  // Load step it moves rows row0 + it*ROWSTEP: the row advance goes into the
+  // scalar base, and the swizzle of those rows equals that of row0 except
+  // for the K chunk bit 3 when ROWSTEP is an odd multiple of 8 (D = 128,
+  // B = 64), so two lane offsets cover every step.
+  const uint32_t koff0 = row0 * rowbytes + (pc0 ^ swz_k(row0, NCH)) * 16;
+  const uint32_t voff0 = row0 * rowbytes + (pc0 ^ swz_v(row0, NCH)) * 16;
+  static_assert(NCH != 16 || ROWSTEP % 8 == 0, "K swizzle period");
+  static_assert(NCH != 8 || ROWSTEP % 16 == 0, "K swizzle period");
+  auto koff_of = [&](int it) {
+    return (NCH == 16 && ((it * ROWSTEP) & 8)) ? (koff0 ^ 128u) : koff0;
+  };
   const uint16_t *kbase = static_cast<const uint16_t *>(a.k);
   const uint16_t *vbase = static_cast<const uint16_t *>(a.v);
   auto issue = [&](int j, int half, int buf) {
-    const int first = j * B + half * SK;                 // first key (local position)
-    const int nrows = min(SK, r.seq_len - first);         // may be <= 0 past the end
+    int first = j * B + half * SK;                       // first key (local position)
+    int nrows = min(SK, r.seq_len - first);               // may be <= 0 past the end
+    if (nrows <= 0) { first = 0; nrows = 1; }             // dummy loads keep the count fixed
     const int64_t e0 = ((r.seq_start + first) * Hkv + r.g) * int64_t(D);
     const uint16_t *kblk = kbase + e0;
     const uint16_t *vblk = vbase + e0;
@@ -195,8 +223,10 @@ void attn_bf16_kernel(AttnArgs a) {
     if (nrows == SK) {
 #pragma unroll
       for (int it = 0; it < LOADS; ++it) {
-        dma16(kblk, koff[it], l0 + it * NT * 16 + buf * TILEB);
-        dma16(vblk, voff[it], l0 + it * NT * 16 + (2 + buf) * TILEB);
+        const char *kb = reinterpret_cast<const char *>(kblk) + size_t(it) * ROWSTEP * rowbytes;
+        const char *vb = reinterpret_cast<const char *>(vblk) + size_t(it) * ROWSTEP * rowbytes;
+        dma16(kb, koff_of(it), l0 + it * NT * 16 + buf * TILEB);
+        dma16(vb, voff0, l0 + it * NT * 16 + (NBUF + buf) * TILEB);
       }
     } else if (nrows > 0) {
 #pragma unroll
@@ -204,7 +234,7 @@ void attn_bf16_kernel(AttnArgs a) {
         const int row = row0 + it * ROWSTEP;
         const uint32_t rb = min(row, nrows - 1) * rowbytes;
         dma16(kblk, rb + (pc0 ^ swz_k(row, NCH)) * 16, l0 + it * NT * 16 + buf * TILEB);
-        dma16(vblk, rb + (pc0 ^ swz_v(row, NCH)) * 16, l0 + it * NT * 16 + (2 + buf) * TILEB);
+        dma16(vblk, rb + (pc0 ^ swz_v(row, NCH)) * 16, l0 + it * NT * 16 + (NBUF + buf) * TILEB);
       }
     }
     // nrows <= 0: the stage lies past the end of the sequence; its keys are
@@ -226,10 +256,10 @@ void attn_bf16_kernel(AttnArgs a) {
     if constexpr (MASK) {
       // nothing visible to this wavefront in this stage (future keys or
       // past the end of the sequence): skip it (wave-uniform)
-      if (key0 > r.i * B + w * QW + QW - 1 || key0 >= r.seq_len) return;
+      if (key0 > r.i * B + w * QW + QW - 1 || key0 >= r.seq_len) { after_s(); return; }
     }
     const char *Kb = lds + buf * TILEB;
-    const char *Vb = lds + (2 + buf) * TILEB;
+    const char *Vb = lds + (NBUF + buf) * TILEB;
     // S^T = K Q^T for keys key0 + 32u .. +31
     f32x16 sacc[KT][QT];
 #pragma unroll
@@ -264,9 +294,7 @@ void attn_bf16_kernel(AttnArgs a) {
       // V^T fragments of this chunk (contraction step hc covers keys
       // kb0 + 4hi + {0..3} and kb0 + 8 + 4hi + {0..3}, kb0 = 32u + 16hc;
       // ds_read_b64_tr_b16 gives lane (n, hi) V[kb0 + 4hi + e][dt*32 + n])
-      bf16x8 vf[2][DT];
-#pragma unroll
-      for (int hc = 0; hc < 2; ++hc) {
+      auto readv = [&](int hc, bf16x8 (&vf)[DT]) {
         const int r0 = u * 32 + 16 * hc + vrow;
         const char *p0 = Vb + r0 * ROWB + vsub;
         const char *p1 = p0 + 8 * ROWB;
@@ -276,10 +304,12 @@ void attn_bf16_kernel(AttnArgs a) {
           const int ch = (dt * 32 + vd) >> 3;
           const v4i16 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(p0 + ((ch ^ sw0) * 16)));
           const v4i16 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(p1 + ((ch ^ sw1) * 16)));
-          vf[hc][dt] = __builtin_bit_cast(bf16x8, (v8i16){v0[0], v0[1], v0[2], v0[3],
-                                                          v1[0], v1[1], v1[2], v1[3]});
+          vf[dt] = __builtin_bit_cast(bf16x8, (v8i16){v0[0], v0[1], v0[2], v0[3],
+                                                      v1[0], v1[1], v1[2], v1[3]});
         }
-      }
+      };
+      bf16x8 vf0[DT], vf1[DT];
+      readv(0, vf0);
       // Online softmax against a lazily moved reference maximum mrun: the
       // weights are exp2((s - mrun) * c); the reference is raised only when
       // some weight of the chunk would exceed 2^8 (their per-lane sum is then
@@ -330,13 +360,16 @@ void attn_bf16_kernel(AttnArgs a) {
       }
       // O^T += V^T P^T
 #pragma unroll
-      for (int hc = 0; hc < 2; ++hc)
+      for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
+        for (int qt = 0; qt < QT; ++qt)
+          oacc[qt][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf0[dt], pf[qt][0], oacc[qt][dt], 0, 0, 0);
+      readv(1, vf1);
 #pragma unroll
-          for (int qt = 0; qt < QT; ++qt)
-            oacc[qt][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[hc][dt], pf[qt][hc],
-                                                                   oacc[qt][dt], 0, 0, 0);
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt)
+          oacc[qt][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf1[dt], pf[qt][1], oacc[qt][dt], 0, 0, 0);
     }
   };
 
@@ -354,30 +387,46 @@ void attn_bf16_kernel(AttnArgs a) {
     return __builtin_amdgcn_readlane(listv, t - chunk);
   };
 
-  // Stage s = 2t + half covers keys [half*SK, half*SK + SK) of entry t and
-  // lives in buffer s & 1.
+  // Stage s covers keys [p*SK, p*SK + SK) of entry s / NPB (p = s % NPB) and
+  // lives in buffer s % NBUF; its DMA is issued NBUF - 1 stages ahead.
   if (nkeep > 0) {
-    int jcur = entry(0);
-    issue(jcur, 0, 0);
-    for (int t = 0; t + 1 < nkeep; ++t) {
-      wait_vm();
+    const int nst = nkeep * NPB;
+    int jq[NBUF];   // block of the stages s .. s + NBUF - 1
+#pragma unroll
+    for (int e = 0; e < NBUF; ++e) jq[e] = 0;
+#pragma unroll
+    for (int e = 0; e < NBUF - 1; ++e)
+      if (e < nst) { jq[e] = entry(e / NPB); issue(jq[e], e % NPB, e); }
+    auto body = [&](int st, auto btag, auto mtag) {
+      constexpr int buf = decltype(btag)::value;
+      // this stage's DMA has landed once at most the later stages' loads
+      // (2 LOADS each, always) are in flight
+      if (NBUF > 2 && st + NBUF - 2 < nst) __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * LOADS * (NBUF - 2)));
+      else wait_vm();
       __syncthreads();
-      // second half of this block
-      step(std::false_type{}, 0, jcur * B, [&] { issue(jcur, 1, 1); });
-      const int jn = entry(t + 1);
-      wait_vm();
-      __syncthreads();
-      // first half of the next block
-      step(std::false_type{}, 1, jcur * B + SK, [&] { issue(jn, 0, 0); });
-      jcur = jn;
-    }
-    wait_vm();
-    __syncthreads();
-    issue(jcur, 1, 1);
-    step(std::true_type{}, 0, jcur * B, [] {});
-    wait_vm();
-    __syncthreads();
-    step(std::true_type{}, 1, jcur * B + SK, [] {});
+      const int key0 = jq[0] * B + (st % NPB) * SK;
+      const int nxt = st + NBUF - 1;
+      auto after = [&] {
+        if (nxt < nst) {
+          jq[NBUF - 1] = entry(nxt / NPB);
+          issue(jq[NBUF - 1], nxt % NPB, (buf + NBUF - 1) % NBUF);
+        }
+      };
+      step(mtag, buf, key0, after);
+#pragma unroll
+      for (int e = 0; e + 1 < NBUF; ++e) jq[e] = jq[e + 1];
+    };
+    // The loop is unrolled over the buffers so that every buffer offset is
+    // a constant.  Stages before the last key block need no mask; the last
+    // block's stages (and up to NBUF - 1 before them) run the masked step.
+    const int nu = nst - NPB;
+    int st = 0;
+    for (; st + NBUF <= nu; st += NBUF)
+      static_for<0, NBUF>([&](auto b) { body(st + decltype(b)::value, b, std::false_type{}); });
+    for (; st < nst; st += NBUF)
+      static_for<0, NBUF>([&](auto b) {
+        if (st + decltype(b)::value < nst) body(st + decltype(b)::value, b, std::true_type{});
+      });
   }
 
   // ---- finalize: O^T lane layout = query n, dims dt*32 + 8(q/4) + 4hi + q%4
