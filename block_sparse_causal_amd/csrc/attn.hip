@@ -119,6 +119,14 @@ constexpr int kStageKeys = 32;   // keys per LDS stage
 template <int B>
 constexpr int stage_bufs() { return B == 128 ? 3 : 2; }
 
+// Lane id (0..63) computed by v_mbcnt in inline assembly: a value the compiler
+// cannot hoist or reuse from an earlier computation.
+__device__ __forceinline__ int opaque_lane_id() {
+  int l;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+  return l;
+}
+
 // f(std::integral_constant<int, I>()) for I = FIRST .. LAST - 1
 template <int FIRST, int LAST, typename F>
 __device__ __forceinline__ void static_for(F &&f) {
@@ -241,10 +249,6 @@ void attn_bf16_kernel(AttnArgs a) {
     // all masked and the buffer is not read
   };
 
-  // lane constants of the V^T operand reads (see the PV step)
-  const int vrow = 4 * hi + ((lane & 15) >> 2);
-  const int vd = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-  const int vsub = ((vd & 7) >> 2) * 8;
 
   // One stage held in buffer `buf`, first key at local position key0.  The
   // S tiles of every 32-key chunk of the stage are issued first, so that the
@@ -253,6 +257,14 @@ void attn_bf16_kernel(AttnArgs a) {
   // Every K and V^T operand read from LDS feeds QT matrix products.
   auto step = [&](auto mask_tag, int buf, int key0, auto &&after_s) {
     constexpr bool MASK = decltype(mask_tag)::value;
+    // The masked step runs only in the short tail; it derives its lane
+    // constants from a lane id the compiler cannot keep from before the main
+    // loop, so that nothing of the tail's addressing stays live through it.
+    const int ln = MASK ? opaque_lane_id() : lane;
+    const int n = ln & 31, hi = ln >> 5;
+    const int vrow = 4 * hi + ((ln & 15) >> 2);
+    const int vd = 16 * ((ln >> 4) & 1) + 4 * (ln & 3);
+    const int vsub = ((vd & 7) >> 2) * 8;
     if constexpr (MASK) {
       // nothing visible to this wavefront in this stage (future keys or
       // past the end of the sequence): skip it (wave-uniform)
@@ -285,7 +297,7 @@ void attn_bf16_kernel(AttnArgs a) {
         // key position <= query position, and inside the sequence
 #pragma unroll
         for (int qt = 0; qt < QT; ++qt) {
-          const int lim = min(qloc[qt], r.seq_len - 1) - (key0 + u * 32 + 4 * hi);
+          const int lim = min(r.i * B + w * QW + qt * 32 + n, r.seq_len - 1) - (key0 + u * 32 + 4 * hi);
 #pragma unroll
           for (int q = 0; q < 16; ++q)
             if (8 * (q >> 2) + (q & 3) > lim) sacc[u][qt][q] = -INFINITY;
