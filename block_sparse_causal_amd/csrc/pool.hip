@@ -6,7 +6,9 @@
 // columns (a "column" is one (head, dim) element of a token row).  Token rows
 // of Q/K/V are contiguous, so a wavefront reads 64 x 16 B = 1 KiB contiguous
 // per token: the kernel is a single coalesced streaming pass over Q, K and V
-// and is bound by HBM bandwidth.  When a tensor has fewer than 256 16-byte
+// and is bound by HBM bandwidth.  The loads are non-temporal: every byte is
+// read once here, and not allocating it in the caches keeps them for the
+// later stages' working set.  When a tensor has fewer than 256 16-byte
 // column vectors (few KV heads), the spare threads take interleaved tokens
 // and the partial sums are combined through LDS.
 //
@@ -101,7 +103,7 @@ __global__ __launch_bounds__(kThreads) void pool_kernel(PoolArgs a) {
       const int t = t0 + ts + u * tsplit;
       ok[u] = active && t < n;
       if (ok[u]) {
-        raw[u] = *reinterpret_cast<const u32x4 *>(src + int64_t(t) * row_bytes);
+        raw[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(src + int64_t(t) * row_bytes));
       } else {
         raw[u] = u32x4{0u, 0u, 0u, 0u};
       }
