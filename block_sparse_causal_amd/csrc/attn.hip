@@ -442,6 +442,39 @@ void attn_bf16_kernel(AttnArgs a) {
   }
 
   // ---- finalize: O^T lane layout = query n, dims dt*32 + 8(q/4) + 4hi + q%4
+  // bf16 output: each wavefront's 32 x D tile goes through LDS (rows
+  // XOR-swizzled by 16-byte chunk), and every store then writes 16 bytes
+  // per lane, whole 2D-byte rows per 16 lanes.
+  if constexpr (OUT_BF16 && QT == 1 && 32 * D * 2 * NW <= 2 * NBUF * TILEB) {
+    __syncthreads();   // every wavefront is done with the stage buffers
+    char *ot = lds + w * (32 * D * 2);
+    const float ltot = lrun[0] + __shfl_xor(lrun[0], 32);
+    const float inv = 1.0f / ltot;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int rg = 0; rg < 4; ++rg) {
+        const int d0 = dt * 32 + 8 * rg + 4 * hi;
+        const uint32_t lo = pack_bf16x2(oacc[0][dt][4 * rg] * inv, oacc[0][dt][4 * rg + 1] * inv);
+        const uint32_t up = pack_bf16x2(oacc[0][dt][4 * rg + 2] * inv, oacc[0][dt][4 * rg + 3] * inv);
+        const int phys = ((d0 >> 3) ^ (n % NCH));
+        *reinterpret_cast<uint2 *>(ot + n * (D * 2) + phys * 16 + (d0 & 4) * 2) = uint2{lo, up};
+      }
+    constexpr int ROWS_PER_STORE = 64 / NCH;      // 4 (d = 128) or 8 (d = 64)
+#pragma unroll
+    for (int it = 0; it < 32 / ROWS_PER_STORE; ++it) {
+      const int row = it * ROWS_PER_STORE + lane / NCH;
+      const int c = lane % NCH;
+      const u32x4 v = *reinterpret_cast<const u32x4 *>(ot + row * (D * 2) + ((c ^ (row % NCH)) * 16));
+      const int qpos = r.i * B + w * QW + row;
+      if (qpos < r.seq_len)
+        *reinterpret_cast<u32x4 *>(static_cast<uint16_t *>(a.out) +
+                                   ((r.seq_start + qpos) * Hq + r.h) * int64_t(D) + c * 8) = v;
+    }
+    if (a.lse && hi == 0 && qloc[0] < r.seq_len)
+      a.lse[int64_t(r.h) * a.T + r.seq_start + qloc[0]] = mrun[0] * a.scale + logf(ltot);
+    return;
+  }
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt) {
     const float ltot = lrun[qt] + __shfl_xor(lrun[qt], 32);
