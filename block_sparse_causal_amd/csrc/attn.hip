@@ -447,6 +447,10 @@ void attn_bf16_kernel(AttnArgs a) {
   // per lane, whole 2D-byte rows per 16 lanes.
   if constexpr (OUT_BF16 && QT == 1 && 32 * D * 2 * NW <= 2 * NBUF * TILEB) {
     __syncthreads();   // every wavefront is done with the stage buffers
+    // lane constants again from an opaque lane id: none of them has to be
+    // kept through the main loop
+    const int lane = opaque_lane_id();
+    const int n = lane & 31, hi = lane >> 5;
     char *ot = lds + w * (32 * D * 2);
     const float ltot = lrun[0] + __shfl_xor(lrun[0], 32);
     const float inv = 1.0f / ltot;
@@ -471,8 +475,9 @@ void attn_bf16_kernel(AttnArgs a) {
         *reinterpret_cast<u32x4 *>(static_cast<uint16_t *>(a.out) +
                                    ((r.seq_start + qpos) * Hq + r.h) * int64_t(D) + c * 8) = v;
     }
-    if (a.lse && hi == 0 && qloc[0] < r.seq_len)
-      a.lse[int64_t(r.h) * a.T + r.seq_start + qloc[0]] = mrun[0] * a.scale + logf(ltot);
+    const int q0 = r.i * B + w * QW + n;
+    if (a.lse && hi == 0 && q0 < r.seq_len)
+      a.lse[int64_t(r.h) * a.T + r.seq_start + q0] = mrun[0] * a.scale + logf(ltot);
     return;
   }
 #pragma unroll
