@@ -20,6 +20,10 @@
 // overlaps the current tile's products), and results leave through a
 // per-wavefront LDS transpose so that every store covers 32 consecutive
 // keys of a row.
+// For bf16 inputs the products run on the bf16 matrix cores with each f32
+// operand split into a bf16 high part and a bf16 remainder (three products,
+// f32 accumulation, relative error about 2^-16 of the product magnitudes);
+// f32 inputs keep the f32 products.
 // Softmax forms: pass 1 keeps an online row max / sum (and the scaled
 // logits, in registers or parked in the output); pass 2 writes
 // exp(x - max) / sum (* vnorm).  The additive form needs no row statistics
@@ -83,7 +87,18 @@ struct TileIO {
   __device__ __forceinline__ float get(int it) const { return t[at(2 * it + (lane >> 5), lane & 31)]; }
 };
 
-template <int D, int MODE>
+// x = hi + lo with hi = bf16(x) and lo = bf16(x - hi) (both round to nearest
+// even): hi.hi' + hi.lo' + lo.hi' equals the f32 product x.x' up to the
+// dropped lo.lo' term and the rounding of lo, both about 2^-16 of |x x'|.
+__device__ __forceinline__ void split_bf16(const f32x8 &x, bf16x8 &h, bf16x8 &l) {
+  h = __builtin_convertvector(x, bf16x8);
+  l = __builtin_convertvector(x - __builtin_convertvector(h, f32x8), bf16x8);
+}
+
+// SPLIT: the pooled dot products as three bf16 matrix products of the split
+// operands (v_mfma_f32_32x32x16_bf16, f32 accumulation), for bf16 inputs;
+// otherwise one f32 product (v_mfma_f32_32x32x2_f32).
+template <int D, int MODE, bool SPLIT>
 __global__ __launch_bounds__(64 * kScoreWaves) void score_kernel(ScoreArgs a) {
   constexpr int HALF = D / 2;
   constexpr int KTILE = 32 * D * 4;          // bytes of one staged 32-row tile
@@ -150,6 +165,19 @@ __global__ __launch_bounds__(64 * kScoreWaves) void score_kernel(ScoreArgs a) {
     qv[4 * c] = x[0]; qv[4 * c + 1] = x[1]; qv[4 * c + 2] = x[2]; qv[4 * c + 3] = x[3];
   }
 
+  // split operand of the bf16 products: contraction chunk c covers dims
+  // hi*HALF + 8c .. + 7, the same dims in both operands
+  bf16x8 qh[SPLIT ? HALF / 8 : 1], ql[SPLIT ? HALF / 8 : 1];
+  if constexpr (SPLIT) {
+#pragma unroll
+    for (int c = 0; c < HALF / 8; ++c) {
+      f32x8 x;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = qv[8 * c + e];
+      split_bf16(x, qh[c], ql[c]);
+    }
+  }
+
   // pass 1: wavefront wv takes key tiles wv, wv + 8, ...; an online row
   // max / sum is kept per lane.  The scaled logits of the first kKeep tiles
   // stay in registers; those of later tiles are parked in the output and
@@ -174,11 +202,25 @@ __global__ __launch_bounds__(64 * kScoreWaves) void score_kernel(ScoreArgs a) {
     wait_lgkm();   // operands in registers: the tile may be refilled
     if (jt + kScoreWaves <= jt_end) load_k(jt + kScoreWaves);
     f32x16 acc = {};
+    if constexpr (SPLIT) {
 #pragma unroll
-    for (int c = 0; c < HALF / 4; ++c)
+      for (int c = 0; c < HALF / 8; ++c) {
+        f32x8 x;
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(kcur[c][e], qv[4 * c + e], acc, 0, 0, 0);
+        for (int e = 0; e < 4; ++e) { x[e] = kcur[2 * c][e]; x[4 + e] = kcur[2 * c + 1][e]; }
+        bf16x8 kh, kl;
+        split_bf16(x, kh, kl);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kh, qh[c], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kh, ql[c], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kl, qh[c], acc, 0, 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int c = 0; c < HALF / 4; ++c)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          acc = __builtin_amdgcn_mfma_f32_32x32x2f32(kcur[c][e], qv[4 * c + e], acc, 0, 0, 0);
+    }
     const int j0 = jt * 32;
     // acc[r] = logit(key j0 + 8(r/4) + 4hi + r%4, query qi)
     if constexpr (MODE == STEM_METRIC_ADDITIVE) {
@@ -262,6 +304,25 @@ __global__ __launch_bounds__(64 * kScoreWaves) void score_kernel(ScoreArgs a) {
   }
 }
 
+template <int D, int MODE>
+void launch_score_d_mode(bool split, dim3 grid, dim3 block, hipStream_t st, const ScoreArgs &a) {
+  if (split) hipLaunchKernelGGL((score_kernel<D, MODE, true>), grid, block, 0, st, a);
+  else hipLaunchKernelGGL((score_kernel<D, MODE, false>), grid, block, 0, st, a);
+}
+
+template <int D>
+void launch_score_d(int mode, bool split, dim3 grid, dim3 block, hipStream_t st, const ScoreArgs &a) {
+  if (mode == STEM_METRIC_ADDITIVE) launch_score_d_mode<D, STEM_METRIC_ADDITIVE>(split, grid, block, st, a);
+  else if (mode == STEM_METRIC_ROUTING) launch_score_d_mode<D, STEM_METRIC_ROUTING>(split, grid, block, st, a);
+  else launch_score_d_mode<D, STEM_METRIC_OUTPUT_AWARE>(split, grid, block, st, a);
+}
+
+void launch_score_kernel(bool d128, int mode, bool split, dim3 grid, dim3 block, hipStream_t st,
+                         const ScoreArgs &a) {
+  if (d128) launch_score_d<128>(mode, split, grid, block, st, a);
+  else launch_score_d<64>(mode, split, grid, block, st, a);
+}
+
 }  // namespace
 
 hipError_t launch_score(const stem_plan_info &in, PlanDev pd, const float *qbar,
@@ -283,22 +344,10 @@ hipError_t launch_score(const stem_plan_info &in, PlanDev pd, const float *qbar,
   dim3 grid(static_cast<unsigned>(tiles * in.num_q_heads));
   const dim3 block(64 * kScoreWaves);
   const bool d128 = in.head_dim == 128;
-  switch (in.metric_mode) {
-    case STEM_METRIC_ADDITIVE:
-      if (d128) hipLaunchKernelGGL((score_kernel<128, STEM_METRIC_ADDITIVE>), grid, block, 0, st, a);
-      else hipLaunchKernelGGL((score_kernel<64, STEM_METRIC_ADDITIVE>), grid, block, 0, st, a);
-      break;
-    case STEM_METRIC_ROUTING:
-      if (d128) hipLaunchKernelGGL((score_kernel<128, STEM_METRIC_ROUTING>), grid, block, 0, st, a);
-      else hipLaunchKernelGGL((score_kernel<64, STEM_METRIC_ROUTING>), grid, block, 0, st, a);
-      break;
-    default:
-      if (d128)
-        hipLaunchKernelGGL((score_kernel<128, STEM_METRIC_OUTPUT_AWARE>), grid, block, 0, st, a);
-      else
-        hipLaunchKernelGGL((score_kernel<64, STEM_METRIC_OUTPUT_AWARE>), grid, block, 0, st, a);
-      break;
-  }
+  const int mode = in.metric_mode == STEM_METRIC_ADDITIVE || in.metric_mode == STEM_METRIC_ROUTING
+                       ? in.metric_mode : STEM_METRIC_OUTPUT_AWARE;
+  const bool split = in.dtype == STEM_BF16;
+  launch_score_kernel(d128, mode, split, grid, block, st, a);
   return hipGetLastError();
 }
 
