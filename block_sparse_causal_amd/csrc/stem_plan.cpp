@@ -99,6 +99,8 @@ extern "C" int stem_plan(const stem_problem *pr, const stem_params *pa,
   // element offsets of Q [T, Hq, d] must fit the kernels' 64-bit math, and
   // block numbers / token numbers are int32 in the plan
   if (nbT > INT32_MAX / 2 || T > INT32_MAX) return STEM_EUNSUPPORTED;
+  // one attention / selection work item per (query head, query block)
+  if (int64_t(pr->num_q_heads) * nbT > INT32_MAX) return STEM_EUNSUPPORTED;
 
   std::vector<int32_t> budget(static_cast<size_t>(nbT));
   int64_t executed = 0;

@@ -139,7 +139,10 @@ typedef struct stem_plan_info {
  * not NULL, writes the plan blob (info->plan_bytes bytes) there.  The
  * caller copies the blob to device memory (16-byte aligned) and passes that
  * copy as plan_dev to the device calls.  Call with plan_host = NULL first to
- * learn plan_bytes.  Returns STEM_ESPACE if capacity < plan_bytes. */
+ * learn plan_bytes.  Returns STEM_ESPACE if capacity < plan_bytes.
+ * Size limits (STEM_EUNSUPPORTED beyond them): at most 4096 blocks in one
+ * sequence (the selection keeps a row's candidates in one wavefront's
+ * registers), T < 2^31 tokens, nbT < 2^30 blocks and Hq * nbT < 2^31. */
 int stem_plan(const stem_problem *problem, const stem_params *params,
               stem_plan_info *info, void *plan_host, int64_t capacity);
 

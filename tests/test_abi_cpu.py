@@ -134,6 +134,9 @@ def test_plan_rejects_bad_arguments():
     assert bad(tau=0.0) == stem.STEM_EINVAL
     assert bad(tau=float("inf")) == stem.STEM_EINVAL
     assert bad(cu_seqlens=[0, 64 * 4097]) == stem.STEM_EUNSUPPORTED
+    # the largest sequence is accepted; work items (Hq * blocks) must fit int32
+    assert stem.stem_plan(**dict(ok, cu_seqlens=[0, 64 * 4096])).info.max_seq_blocks == 4096
+    assert bad(cu_seqlens=[0, 64 * 4096], num_q_heads=2 ** 20, num_kv_heads=1) == stem.STEM_EUNSUPPORTED
     assert bad(budget_mode="cosine") == stem.STEM_EINVAL
     assert bad(metric="oam") == stem.STEM_EINVAL
     assert bad(metric="additive", beta=-1.0) == stem.STEM_EINVAL

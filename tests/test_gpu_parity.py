@@ -208,8 +208,9 @@ def test_select_long_budget_and_wide_ties():
 # ----------------------------------------------------------------- full size
 
 
-def _full_size(name: str, n_attn_rows: int, **params):
-    w = syn.WORKLOADS[name].replace(**params)
+def _full_size(name, n_attn_rows: int, **params):
+    w = (syn.WORKLOADS[name] if isinstance(name, str) else name).replace(**params)
+    name = w.name
     H.log(f"case full-size {name}: generating inputs")
     r = H.GpuRun(w, out_dtype="bf16")
     H.log(f"case full-size {name}: GPU done, checking pooled values")
@@ -257,3 +258,14 @@ def test_full_size_additive_metric_linear_budget():
     _cuda()
     _full_size("llama3-8b-32k-b64", 64, metric="additive", beta=0.2, budget_mode="linear",
                k_start=24.0, mu=0.7)
+
+
+@pytest.mark.timeout(900)
+def test_maximum_sequence_length():
+    """The longest sequence the library accepts (4096 blocks of 64 tokens):
+    the selection then holds 4094 candidates per row (64 per lane), and the
+    metric has 128 key tiles per row tile."""
+    _cuda()
+    w = syn.custom([64 * 4096], 2, 1, 64, "bf16", 64, sink_blocks=2, k_min=8, rho0=0.5,
+                   tau=64.0, seed=61).replace(name="max-seq-4096-blocks")
+    _full_size(w, 48)
