@@ -17,8 +17,8 @@
 //                 lanes).
 // bf16 inputs use v_mfma_f32_32x32x16_bf16 with f32 accumulation; f32 inputs
 // use v_mfma_f32_32x32x2_f32.  The token-level causal mask is applied only
-// when the key block is the diagonal block; a final partial block is
-// zero-filled in LDS and masked.
+// when the key block is the diagonal block; the missing rows of a final
+// partial block repeat its last valid row in LDS and are masked.
 //
 // Grid order: workgroups are issued round-robin over the 8 XCDs of the chip,
 // each with its own L2.  Work item L is placed so that contiguous ranges of
@@ -220,10 +220,14 @@ void attn_bf16_kernel(AttnArgs a) {
   };
   const uint16_t *kbase = static_cast<const uint16_t *>(a.k);
   const uint16_t *vbase = static_cast<const uint16_t *>(a.v);
-  auto issue = [&](int j, int half, int buf) {
-    int first = j * B + half * SK;                       // first key (local position)
+  // Stage `part` of block j into buffer `buf`.  Every call issues exactly
+  // 2 LOADS DMA instructions (the stage waits count on it): a stage that lies
+  // past the end of the sequence (keys all masked, buffer not read) loads
+  // the sequence's first row instead.
+  auto issue = [&](int j, int part, int buf) {
+    int first = j * B + part * SK;                       // first key (local position)
     int nrows = min(SK, r.seq_len - first);               // may be <= 0 past the end
-    if (nrows <= 0) { first = 0; nrows = 1; }             // dummy loads keep the count fixed
+    if (nrows <= 0) { first = 0; nrows = 1; }
     const int64_t e0 = ((r.seq_start + first) * Hkv + r.g) * int64_t(D);
     const uint16_t *kblk = kbase + e0;
     const uint16_t *vblk = vbase + e0;
@@ -245,16 +249,14 @@ void attn_bf16_kernel(AttnArgs a) {
         dma16(vblk, rb + (pc0 ^ swz_v(row, NCH)) * 16, l0 + it * NT * 16 + (NBUF + buf) * TILEB);
       }
     }
-    // nrows <= 0: the stage lies past the end of the sequence; its keys are
-    // all masked and the buffer is not read
   };
 
 
-  // One stage held in buffer `buf`, first key at local position key0.  The
-  // S tiles of every 32-key chunk of the stage are issued first, so that the
-  // matrix cores work on chunk u+1 while the vector unit runs the softmax of
-  // chunk u, and the PV products of chunk u overlap the softmax of chunk u+1.
-  // Every K and V^T operand read from LDS feeds QT matrix products.
+  // One stage held in buffer `buf`, first key at local position key0: the S
+  // tile, the next stages' DMA, the softmax and the PV products.  Three
+  // wavefronts of independent workgroups share each SIMD, so one's softmax
+  // and LDS reads overlap another's matrix products.  Every K and V^T
+  // operand read from LDS feeds QT matrix products.
   auto step = [&](auto mask_tag, int buf, int key0, auto &&after_s) {
     constexpr bool MASK = decltype(mask_tag)::value;
     // The masked step runs only in the short tail; it derives its lane
@@ -444,7 +446,7 @@ void attn_bf16_kernel(AttnArgs a) {
   // ---- finalize: O^T lane layout = query n, dims dt*32 + 8(q/4) + 4hi + q%4
   // bf16 output: each wavefront's 32 x D tile goes through LDS (rows
   // XOR-swizzled by 16-byte chunk), and every store then writes 16 bytes
-  // per lane, whole 2D-byte rows per 16 lanes.
+  // per lane, one whole 2D-byte row per D/8 lanes.
   if constexpr (OUT_BF16 && QT == 1 && 32 * D * 2 * NW <= 2 * NBUF * TILEB) {
     __syncthreads();   // every wavefront is done with the stage buffers
     // lane constants again from an opaque lane id: none of them has to be
