@@ -19,6 +19,11 @@ int check_info(const stem_plan_info *in, const void *plan_dev) {
   if (in->block != 64 && in->block != 128) return STEM_EUNSUPPORTED;
   if (in->dtype != STEM_F32 && in->dtype != STEM_BF16) return STEM_EUNSUPPORTED;
   if (in->total_blocks < 0 || in->total_tokens < 0) return STEM_EINVAL;
+  // the size limits stem_plan enforces (a plan edited afterwards could exceed them)
+  if (in->total_tokens > INT32_MAX || in->total_blocks > INT32_MAX / 2 ||
+      int64_t(in->num_q_heads) * in->total_blocks > INT32_MAX ||
+      in->max_seq_blocks > STEM_MAX_SEQ_BLOCKS)
+    return STEM_EUNSUPPORTED;
   if (in->metric_mode < STEM_METRIC_OUTPUT_AWARE || in->metric_mode > STEM_METRIC_ROUTING)
     return STEM_EINVAL;
   if (in->total_blocks > 0 && (!plan_dev || !aligned(plan_dev, 16))) return STEM_EINVAL;
@@ -63,7 +68,6 @@ extern "C" int stem_select(const stem_plan_info *in, const void *plan_dev, const
   if (in->total_blocks == 0) return STEM_OK;
   if (!scores || !idx || !count || in->kmax < 1) return STEM_EINVAL;
   if (!aligned(scores, 4) || !aligned(idx, 4) || !aligned(count, 4)) return STEM_EINVAL;
-  if (in->max_seq_blocks > STEM_MAX_SEQ_BLOCKS) return STEM_EUNSUPPORTED;
   return hip_status(launch_select(*in, make_plan_dev(*in, plan_dev), scores, idx, count,
                                   static_cast<hipStream_t>(stream)));
 }

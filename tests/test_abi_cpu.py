@@ -182,4 +182,14 @@ def test_device_calls_reject_bad_arguments_before_any_launch():
     bad = stem.stem_plan_info.from_buffer_copy(info)
     bad.magic = 0
     assert L.stem_score(ctypes.byref(bad), P, P, P, P, P, None) == stem.STEM_EINVAL
+    # a plan edited past the size limits is refused by every device call
+    for field, value in [("max_seq_blocks", 5000), ("total_blocks", 1 << 30),
+                         ("num_q_heads", 1 << 24)]:
+        big = stem.stem_plan_info.from_buffer_copy(info)
+        setattr(big, field, value)
+        if field == "num_q_heads":
+            big.num_kv_heads = 1
+        assert L.stem_select(ctypes.byref(big), P, P, P, P, None) == stem.STEM_EUNSUPPORTED, field
+        assert L.stem_sparse_attn(ctypes.byref(big), P, P, P, P, P, P, P, 0, None, None) == \
+            stem.STEM_EUNSUPPORTED, field
     assert stem.status_str(stem.STEM_EUNSUPPORTED) == "unsupported configuration"
