@@ -184,7 +184,7 @@ def test_device_calls_reject_bad_arguments_before_any_launch():
     assert L.stem_score(ctypes.byref(bad), P, P, P, P, P, None) == stem.STEM_EINVAL
     # a plan edited past the size limits is refused by every device call
     for field, value in [("max_seq_blocks", 5000), ("total_blocks", 1 << 30),
-                         ("num_q_heads", 1 << 24)]:
+                         ("num_q_heads", 1 << 30)]:
         big = stem.stem_plan_info.from_buffer_copy(info)
         setattr(big, field, value)
         if field == "num_q_heads":
