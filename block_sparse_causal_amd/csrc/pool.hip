@@ -15,7 +15,7 @@
 // Outputs: qbar [Hq, nbT, d] and kbar [Hkv, nbT, d] hold block means
 // (f32); vnorm [Hkv, nbT] holds the mean (or max) over the block's tokens of
 // the per-token L2 norm of V, computed in f32 from the 16 B slices of one
-// head row with a butterfly across the lanes that hold that row.
+// head row, summed across the lanes that hold that row by a DPP scan.
 #include "stem_device.h"
 
 namespace stem {
@@ -55,11 +55,33 @@ struct Vec<false> {
   }
 };
 
+// Data-parallel-primitive (DPP) move of x from another lane, 0 where the
+// source lies outside the row (16 lanes) or the row is masked off.
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ float dpp(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL,
+                                                               ROW_MASK, 0xF, true));
+}
+
+// Sum of x over each group of L consecutive lanes (L = 8, 16 or 32), left in
+// the group's last lane: an inclusive scan within 16-lane rows (row_shr by
+// 1, 2, 4, 8) and, for L = 32, row 15's partial broadcast into the next row.
+template <int L>
+__device__ __forceinline__ float group_sum_last(float x) {
+  x += dpp<0x111>(x);
+  x += dpp<0x112>(x);
+  x += dpp<0x114>(x);
+  if constexpr (L >= 16) x += dpp<0x118>(x);
+  if constexpr (L >= 32) x += dpp<0x142, 0xA>(x);
+  return x;
+}
+
 template <bool BF16, int D>
 __global__ __launch_bounds__(kThreads) void pool_kernel(PoolArgs a) {
   constexpr int VEC = Vec<BF16>::N;
   constexpr int ESZ = BF16 ? 2 : 4;
   constexpr int LANES_PER_HEAD = D / VEC;  // 8, 16 or 32: divides 64
+  static_assert(LANES_PER_HEAD == 8 || LANES_PER_HEAD == 16 || LANES_PER_HEAD == 32, "lanes per head row");
   __shared__ float red[kThreads * (VEC + 1)];
 
   const int tid = threadIdx.x;
@@ -116,10 +138,9 @@ __global__ __launch_bounds__(kThreads) void pool_kernel(PoolArgs a) {
         float sq = 0.f;
 #pragma unroll
         for (int e = 0; e < VEC; ++e) sq = fmaf(f[e], f[e], sq);
-        // butterfly over the lanes holding this head's row (uniform trip
-        // count: every lane of the wavefront takes part)
-#pragma unroll
-        for (int m = 1; m < LANES_PER_HEAD; m <<= 1) sq += __shfl_xor(sq, m);
+        // sum over the lanes holding this head's row, in its last lane
+        // (every lane of the wavefront takes part)
+        sq = group_sum_last<LANES_PER_HEAD>(sq);
         const float nrm = sqrtf(sq);
         if (ok[u]) nacc = a.vnorm_max ? fmaxf(nacc, nrm) : nacc + nrm;
       } else {
@@ -147,7 +168,7 @@ __global__ __launch_bounds__(kThreads) void pool_kernel(PoolArgs a) {
   const int d0 = col % D;
   const float inv_n = 1.0f / float(n);
   if (tensor == 2) {
-    if (d0 == 0) a.vnorm[int64_t(h) * a.nbT + b] = a.vnorm_max ? nacc : nacc * inv_n;
+    if (d0 == D - VEC) a.vnorm[int64_t(h) * a.nbT + b] = a.vnorm_max ? nacc : nacc * inv_n;
     return;
   }
   float *dst = (tensor == 0 ? a.qbar : a.kbar) + (int64_t(h) * a.nbT + b) * D + d0;
