@@ -17,6 +17,10 @@ Reported (one JSON line on stdout, progress on stderr):
   stages      per-stage ms; effective TFLOP/s of attention and of the step
   dense       the same attention kernel with every causal block kept (the
               dense causal comparator) and the speed-up over it
+  ceilings    the chip's matrix-core rate on random and on constant bf16
+              operands and its streaming HBM read rate, re-measured by the
+              library's probe kernels (the published peaks assume neither
+              the power limit nor the memory system's efficiency)
   cpu_baseline  the CPU oracle timed on a bounded sample and scaled up
 """
 from __future__ import annotations
@@ -160,6 +164,39 @@ def cpu_baseline(w, x):
                 host_cpus=len(os.sched_getaffinity(0)))
 
 
+def measure_ceilings(reps: int = 5):
+    """Best-of-reps rates of the probe kernels, timed with HIP events."""
+    import torch
+    from block_sparse_causal_amd import stem
+    st = torch.cuda.current_stream()
+    sink = torch.empty(4096, dtype=torch.float32, device="cuda")
+
+    def best(launch):
+        launch()
+        torch.cuda.synchronize()
+        ms = []
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(st)
+            work = launch()
+            b.record(st)
+            b.synchronize()
+            ms.append(a.elapsed_time(b))
+        return work, min(ms)
+
+    out = {}
+    for key, rnd in (("mfma_bf16_random_tflops", True), ("mfma_bf16_constant_tflops", False)):
+        flops, ms = best(lambda: stem.stem_probe_mfma(rnd, sink, st))
+        out[key] = round(flops / (ms * 1e-3) / 1e12, 1)
+    buf = torch.empty(1 << 29, dtype=torch.int64, device="cuda").fill_(0x0123456789)  # 4 GiB
+    wsink = torch.zeros(buf.numel() * 8 // 65536, dtype=torch.int32, device="cuda")
+    nbytes, ms = best(lambda: stem.stem_probe_hbm_read(buf, wsink, st))
+    out["hbm_read_gbs"] = round(nbytes / (ms * 1e-3) / 1e9, 1)
+    del buf
+    torch.cuda.empty_cache()
+    return out
+
+
 def copy_calibration(nbytes: int = 1 << 30):
     """One device-to-device copy of a known size, for scaling the hardware
     byte counters of a profiling run (its kernel reads and writes nbytes)."""
@@ -230,6 +267,8 @@ def main():
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--no-ceilings", action="store_true",
+                    help="skip the matrix-core and HBM probe kernels")
     ap.add_argument("--sweep", action="store_true",
                     help="latency against context length (8K..128K), Stem vs dense")
     args = ap.parse_args()
@@ -326,6 +365,14 @@ def main():
                            "tflops": round(dflops / (dms * 1e-3) / 1e12, 2),
                            "speedup_vs_stem_step": round(dms / step_ms, 2)}
         log(f"dense attention {dms:.2f} ms -> speed-up {dms / step_ms:.2f}x")
+
+    if not args.no_ceilings:
+        log("probe kernels: matrix-core and HBM ceilings")
+        c = measure_ceilings()
+        c["attn_frac_of_random_mfma"] = round(achieved / c["mfma_bf16_random_tflops"], 4)
+        c["pool_frac_of_hbm_read"] = round(result["hbm_gbs"]["pool"] / c["hbm_read_gbs"], 4)
+        result["ceilings"] = c
+        log(f"ceilings: {c}")
 
     if args.copy_calibration:
         copy_calibration()

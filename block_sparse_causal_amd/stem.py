@@ -96,6 +96,9 @@ _SIGS = {
     "stem_sparse_attn": (ctypes.c_int, [ctypes.POINTER(stem_plan_info), _P, _P, _P, _P, _P, _P,
                                         _P, ctypes.c_int32, _P, _P]),
     "stem_status_str": (ctypes.c_char_p, [ctypes.c_int]),
+    "stem_probe_mfma": (ctypes.c_int, [ctypes.c_int32, _P, ctypes.c_int64,
+                                       ctypes.POINTER(ctypes.c_double), _P]),
+    "stem_probe_hbm_read": (ctypes.c_int, [_P, ctypes.c_int64, _P, ctypes.c_int64, _P]),
 }
 
 
@@ -292,6 +295,33 @@ def stem_sparse_attn(plan: Plan, q, k, v, idx, count, out, lse=None, stream=None
            lib().stem_sparse_attn(ctypes.byref(i), plan.dev_ptr, q.data_ptr(), k.data_ptr(),
                                   v.data_ptr(), idx.data_ptr(), count.data_ptr(), out.data_ptr(),
                                   odt, _ptr(lse), _stream(stream)))
+
+
+def stem_probe_mfma(random_operands: bool, sink, stream=None) -> float:
+    """Launch the matrix-core probe; returns the launch's flop count.  sink:
+    float32 device tensor (4096 elements suffice)."""
+    import torch
+    _need(sink, "sink", torch.float32, (sink.numel(),))
+    flops = ctypes.c_double()
+    _check("stem_probe_mfma",
+           lib().stem_probe_mfma(int(bool(random_operands)), sink.data_ptr(), sink.numel(),
+                                 ctypes.byref(flops), _stream(stream)))
+    return flops.value
+
+
+def stem_probe_hbm_read(buf, sink, stream=None) -> int:
+    """Launch the streaming-read probe over the bytes of the contiguous
+    device tensor buf; returns the bytes read.  sink: int32 device tensor
+    of at least ceil(bytes / 65536) elements (one per 64 KiB chunk)."""
+    import torch
+    _need(sink, "sink", torch.int32, (sink.numel(),))
+    if not buf.is_cuda or not buf.is_contiguous():
+        raise ValueError("buf must be a contiguous GPU tensor")
+    nbytes = buf.numel() * buf.element_size()
+    _check("stem_probe_hbm_read",
+           lib().stem_probe_hbm_read(buf.data_ptr(), nbytes, sink.data_ptr(), sink.numel(),
+                                     _stream(stream)))
+    return nbytes
 
 
 # ---------------------------------------------------------------- conveniences

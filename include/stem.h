@@ -200,6 +200,34 @@ int stem_sparse_attn(const stem_plan_info *info, const void *plan_dev,
                      const int32_t *idx, const int32_t *count,
                      void *out, int32_t out_dtype, float *lse, void *stream);
 
+/* Measurement probes (not part of the prefill path): they re-measure, on the
+ * device at hand, the ceilings the kernels above are compared with.  Each
+ * launches one kernel on `stream` and returns at once; the caller times the
+ * launch (HIP events on the same stream).  They allocate nothing.
+ *
+ * stem_probe_mfma - back-to-back bf16 v_mfma_f32_32x32x16 on every SIMD of
+ * the current device, four independent accumulators per wavefront.  With
+ * random_operands != 0 the operands are random bf16 values in [-1, 1),
+ * rotating among four sets, else small constants: the matrix-core rate
+ * depends on the operand bit activity (the chip's power limit).  *flops
+ * receives the multiply-add work of the launch (2 per multiply-add).  sink
+ * is device memory of at least sink_floats f32 (256 x 16 suffice up to 256
+ * CUs), overwritten with a value per workgroup.  STEM_EINVAL if a pointer is
+ * NULL or sink_floats is smaller than the launch's workgroup count. */
+int stem_probe_mfma(int32_t random_operands, float *sink, int64_t sink_floats,
+                    double *flops, void *stream);
+
+/* stem_probe_hbm_read - one pass of 16-byte non-temporal loads over the
+ * `bytes` bytes at buf (device memory, 16-byte aligned, bytes a positive
+ * multiple of 16), the access pattern of the pooling kernel, each workgroup
+ * reading one contiguous 64 KiB chunk.  sink is device memory of at least
+ * sink_words uint32, sink_words >= ceil(bytes / 65536): word c receives the
+ * XOR of the 32-bit words of chunk c, so the XOR of those sink words equals
+ * the XOR of the buffer's words.  STEM_EINVAL on a NULL pointer, a bad size,
+ * a short sink or misalignment. */
+int stem_probe_hbm_read(const void *buf, int64_t bytes, uint32_t *sink, int64_t sink_words,
+                        void *stream);
+
 /* Human-readable text of a stem_status value. */
 const char *stem_status_str(int status);
 
