@@ -41,7 +41,10 @@ reading taken is stated in the function that implements it:
     blocks, with the token-level causal mask applied inside the diagonal
     block only;
   * a final partial block (sequence length not a multiple of the block size)
-    pools over its valid tokens only.
+    pools over its valid tokens only;
+  * anti-diagonal sampling ([fr] 2.C step 1), the alternative block logit:
+    the log-mean-exp of anti-diagonal samples of the token logits, in place
+    of the pooled logit (reading stated above antidiag_row_logits).
 """
 from __future__ import annotations
 
@@ -171,14 +174,30 @@ def score_row_values(qbar: np.ndarray, kbar: np.ndarray, w: np.ndarray,
     g = h // (qbar.shape[0] // kbar.shape[0])
     b0 = int(cu_blocks[s])
     logits = kbar[g, b0:b0 + i + 1, :] @ qbar[h, b0 + i, :] * (1.0 / math.sqrt(head_dim))
-    wj = w[g, b0:b0 + i + 1].astype(np.float64)
+    return metric_from_logits(logits, w[g, b0:b0 + i + 1], metric, beta)
+
+
+def metric_from_logits(logits: np.ndarray, wj: np.ndarray, metric: str = "output_aware",
+                       beta: float = 0.5) -> np.ndarray:
+    """The metric of one row from its block logits s_i0 .. s_ii and the key
+    blocks' V magnitudes (the three forms listed in score).  A row whose
+    logits are all -inf (no sampled evidence, see antidiag_row_logits) gets
+    routing weight 0 everywhere."""
+    if metric not in METRICS:
+        raise ValueError(metric)
+    logits = np.asarray(logits, dtype=np.float64)
+    wj = np.asarray(wj, dtype=np.float64)
     if metric == "additive":
         # log(0) = -inf, so a block of zero values gets no bonus
         with np.errstate(divide="ignore"):
             lw2 = np.log(wj * wj)
         return logits + beta * np.maximum(0.0, lw2)
-    p = np.exp(logits - logits.max())
-    p /= p.sum()
+    top = logits.max()
+    if not np.isfinite(top):
+        p = np.zeros_like(logits)
+    else:
+        p = np.exp(logits - top)
+        p /= p.sum()
     return p if metric == "routing" else p * wj
 
 
@@ -186,6 +205,107 @@ def score_row(m: np.ndarray, cu_blocks: np.ndarray, h: int, s: int, i: int) -> n
     offs, _ = score_offsets(cu_blocks)
     row0 = int(offs[s]) + tri(i)
     return m[h, row0:row0 + i + 1]
+
+
+# ----------------------------------------------------------------------------
+# Anti-diagonal sampled block logits ([fr] 2.C, step 1: the block metric is
+# computed with anti-diagonal sampling, for efficiency; the page gives no
+# stride and no formula).  Reading taken here:
+#   * a sequence's tokens are cut into groups of `stride` consecutive
+#     positions (the last group may be short); stride divides the block size,
+#     so block i holds groups i*B/stride .. (i+1)*B/stride - 1;
+#   * the sample of query group r and key group c is the anti-diagonal of
+#     their stride x stride tile of token logits: query position
+#     r*stride + stride-1-u with key position c*stride + u, u = 0..stride-1,
+#     keeping only pairs whose two tokens exist and whose key does not come
+#     after the query; the sample value is the mean of q.k/sqrt(d) over
+#     those pairs (a group pair with no such pair gives no sample);
+#   * the block logit t_ij is the log of the mean of exp(sample) over the
+#     samples of query block i and key block j (-inf if there are none),
+#     so softmax_j(t_ij) is the share of query block i's sampled attention
+#     mass that lands on key block j;
+#   * t_ij then takes the place of the pooled logit s_ij in the metric,
+#     unchanged otherwise (metric_from_logits).
+# With stride 1 every causal token pair is sampled and t_ij is the exact
+# log-mean-exp of the block pair's token logits.
+
+
+def antidiag_row_logits(q: np.ndarray, k: np.ndarray, cu_seqlens: Sequence[int],
+                        block: int, stride: int, h: int, s: int, i: int) -> np.ndarray:
+    """t_i0 .. t_ii (float64) for query head h, sequence s, local query
+    block i; q [T, Hq, d], k [T, Hkv, d]."""
+    if stride < 1 or block % stride:
+        raise ValueError("stride must divide the block size")
+    T, Hq, d = q.shape
+    g = h // (Hq // k.shape[1])
+    t0 = int(cu_seqlens[s])
+    n = int(cu_seqlens[s + 1]) - t0
+    gpb = block // stride
+    ng = -(-n // stride)
+    rows = np.arange(i * gpb, min((i + 1) * gpb, ng))
+    cols = np.arange(0, min((i + 1) * gpb, ng))
+    u = np.arange(stride)
+    qpos = rows[:, None] * stride + (stride - 1) - u[None, :]      # [R, stride]
+    kpos = cols[:, None] * stride + u[None, :]                     # [C, stride]
+    ok = ((qpos[:, None, :] < n) & (kpos[None, :, :] < n) &
+          (kpos[None, :, :] <= qpos[:, None, :]))                  # [R, C, stride]
+    qi = np.minimum(qpos, n - 1)
+    kj = np.minimum(kpos, n - 1)
+    # token logits of the rows' query tokens against the keys up to block i
+    qt = q[t0:t0 + n, h, :].astype(np.float64)
+    kt = k[t0:t0 + n, g, :].astype(np.float64)
+    lq0, lq1 = int(qi.min()), int(qi.max()) + 1
+    lk1 = int(kj.max()) + 1
+    L = (qt[lq0:lq1] @ kt[:lk1].T) / math.sqrt(d)
+    vals = L[(qi - lq0)[:, None, :], kj[None, :, :]]
+    cnt = ok.sum(axis=2)
+    tot = np.where(ok, vals, 0.0).sum(axis=2)
+    out = np.full(i + 1, -np.inf)
+    for j in range(i + 1):
+        sel = (cols >= j * gpb) & (cols < (j + 1) * gpb)
+        c = cnt[:, sel]
+        x = tot[:, sel][c > 0] / c[c > 0]
+        if x.size:
+            top = x.max()
+            out[j] = top + math.log(np.exp(x - top).mean())
+    return out
+
+
+def antidiag_block_logits(q: np.ndarray, k: np.ndarray, cu_seqlens: Sequence[int],
+                          block: int, stride: int) -> np.ndarray:
+    """Packed lower-triangular anti-diagonal block logits t [Hq, tri_total]."""
+    cu_blocks = block_layout(cu_seqlens, block)
+    offs, total = score_offsets(cu_blocks)
+    Hq = q.shape[1]
+    out = np.full((Hq, total), -np.inf)
+    for h in range(Hq):
+        for s in range(len(cu_blocks) - 1):
+            for i in range(int(cu_blocks[s + 1]) - int(cu_blocks[s])):
+                row0 = int(offs[s]) + tri(i)
+                out[h, row0:row0 + i + 1] = antidiag_row_logits(q, k, cu_seqlens, block,
+                                                                stride, h, s, i)
+    return out
+
+
+def score_antidiag(q: np.ndarray, k: np.ndarray, w: np.ndarray, cu_seqlens: Sequence[int],
+                   block: int, stride: int, metric: str = "output_aware",
+                   beta: float = 0.5) -> np.ndarray:
+    """The metric with anti-diagonal sampled block logits in place of the
+    pooled ones: packed m [Hq, tri_total] (float64)."""
+    cu_blocks = block_layout(cu_seqlens, block)
+    offs, total = score_offsets(cu_blocks)
+    t = antidiag_block_logits(q, k, cu_seqlens, block, stride)
+    Hq = q.shape[1]
+    G = Hq // k.shape[1]
+    out = np.zeros((Hq, total))
+    for h in range(Hq):
+        for s in range(len(cu_blocks) - 1):
+            b0 = int(cu_blocks[s])
+            for i in range(int(cu_blocks[s + 1]) - b0):
+                row0 = int(offs[s]) + tri(i)
+                out[h, row0:row0 + i + 1] = metric_from_logits(
+                    t[h, row0:row0 + i + 1], w[h // G, b0:b0 + i + 1], metric, beta)
+    return out
 
 
 # ----------------------------------------------------------------------------
@@ -409,15 +529,20 @@ def budgets_for(cu_blocks: np.ndarray, sink_blocks: int, k_min: int,
 
 def prefill(q, k, v, cu_seqlens, block, sink_blocks, k_min, rho0, tau,
             vnorm_mode: str = "mean", metric: str = "output_aware", beta: float = 0.5,
-            budget_mode: str = "exp", k_start: float = 0.0, mu: float = 0.0):
+            budget_mode: str = "exp", k_start: float = 0.0, mu: float = 0.0,
+            score_stride: Optional[int] = None):
     """pool -> score -> budget -> select -> attention.  Returns a dict of
-    every intermediate (float64 / int)."""
+    every intermediate (float64 / int).  With score_stride set, the metric
+    takes the anti-diagonal sampled block logits (score_antidiag)."""
     d = q.shape[2]
     cub = block_layout(cu_seqlens, block)
     qbar = pool_mean(q, cu_seqlens, block)
     kbar = pool_mean(k, cu_seqlens, block)
     w = pool_vnorm(v, cu_seqlens, block, vnorm_mode)
-    m = score(qbar, kbar, w, cub, d, metric, beta)
+    if score_stride is None:
+        m = score(qbar, kbar, w, cub, d, metric, beta)
+    else:
+        m = score_antidiag(q, k, w, cu_seqlens, block, score_stride, metric, beta)
     bud = budgets_for(cub, sink_blocks, k_min, rho0, tau, budget_mode, k_start, mu)
     idx, cnt = select(m, cub, bud, sink_blocks)
     o, lse = sparse_attn(q, k, v, idx, cnt, cu_seqlens, block)
