@@ -85,14 +85,20 @@ def upload(x, device="cuda"):
     return tuple(torch.from_numpy(a).to(device) for a in (x.q, x.k, x.v))
 
 
-def time_path(plan, q, k, v, bufs, steps: int, warmup: int, vnorm_mode=0):
-    """Run warmup + timed steps; return (ms_per_step wall, per-stage ms lists)."""
+def time_path(plan, q, k, v, bufs, steps: int, warmup: int, vnorm_mode=0, score_stride=None):
+    """Run warmup + timed steps; return (ms_per_step wall, per-stage ms lists).
+    With score_stride set the metric stage is stem_score_antidiag."""
     import torch
     from block_sparse_causal_amd import stem
     st = torch.cuda.current_stream()
+    if score_stride is None:
+        score = lambda: stem.stem_score(plan, bufs.qbar, bufs.kbar, bufs.vnorm, bufs.scores, st)
+    else:
+        score = lambda: stem.stem_score_antidiag(plan, q, k, bufs.vnorm, score_stride, bufs.scores,
+                                                 st)
     calls = [
         lambda: stem.stem_pool(plan, q, k, v, bufs.qbar, bufs.kbar, bufs.vnorm, vnorm_mode, st),
-        lambda: stem.stem_score(plan, bufs.qbar, bufs.kbar, bufs.vnorm, bufs.scores, st),
+        score,
         lambda: stem.stem_select(plan, bufs.scores, bufs.idx, bufs.count, st),
         lambda: stem.stem_sparse_attn(plan, q, k, v, bufs.idx, bufs.count, bufs.out, bufs.lse, st),
     ]
@@ -113,6 +119,19 @@ def time_path(plan, q, k, v, bufs, steps: int, warmup: int, vnorm_mode=0):
     stage = [[ev[s][n].elapsed_time(ev[s][n + 1]) for s in range(steps)] for n in range(len(calls))]
     total = [ev[s][0].elapsed_time(ev[s][len(calls)]) for s in range(steps)]
     return wall, stage, total
+
+
+def antidiag_flops(w, stride: int) -> float:
+    """Algorithmic FLOPs of the anti-diagonal samples: 2 d per sampled token
+    pair (key not after query, both tokens present), every query head."""
+    pairs = 0
+    for n in w.seqlens:
+        ng = -(-n // stride)
+        half = (stride + 1) // 2
+        for r in range(ng):
+            m = min(stride, n - r * stride)
+            pairs += r * m + max(0, min(m - 1, half - 1) - (stride - m) + 1)
+    return 2.0 * w.head_dim * pairs * w.num_q_heads
 
 
 def dense_attention_ms(w, q, k, v, reps: int):
@@ -267,6 +286,9 @@ def main():
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--score-stride", type=int, default=None,
+                    help="metric from anti-diagonal samples of the token logits at this stride "
+                         "(stem_score_antidiag) instead of the pooled blocks")
     ap.add_argument("--no-ceilings", action="store_true",
                     help="skip the matrix-core and HBM probe kernels")
     ap.add_argument("--sweep", action="store_true",
@@ -298,7 +320,8 @@ def main():
     torch.cuda.synchronize()
 
     log(f"timing {args.warmup} warmup + {args.steps} steps")
-    wall_ms, stage, total = time_path(plan, q, k, v, bufs, args.steps, args.warmup)
+    wall_ms, stage, total = time_path(plan, q, k, v, bufs, args.steps, args.warmup,
+                                      score_stride=args.score_stride)
     names = ["pool", "score", "select", "attn"]
     stage_ms = {n: float(np.mean(s)) for n, s in zip(names, stage)}
     step_ms = float(np.mean(total))
@@ -356,6 +379,16 @@ def main():
                     "peak": PEAK_HBM_GBS},
         "wall_ms_per_step": round(wall_ms, 4),
     }
+    if args.score_stride is not None:
+        af = antidiag_flops(w, args.score_stride)
+        ach = af / (stage_ms["score"] * 1e-3) / 1e12
+        result["config"]["score"] = f"antidiag stride {args.score_stride}"
+        # the score stage is stem_score_antidiag: the sample products plus
+        # the row-softmax kernel
+        result["antidiag"] = {"bound": "mfma", "achieved": round(ach, 2), "peak": peak,
+                              "unit": "TFLOP/s", "frac": round(ach / peak, 4),
+                              "flop_per_launch": af, "avg_launch_ms": round(stage_ms["score"], 4)}
+        log(f"antidiag stride {args.score_stride}: {stage_ms['score']:.3f} ms, {ach:.1f} TFLOP/s")
     del bufs
 
     if not args.no_dense:

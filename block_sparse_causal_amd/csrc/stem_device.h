@@ -94,6 +94,12 @@ hipError_t launch_pool(const stem_plan_info &in, PlanDev pd, const void *q,
 hipError_t launch_score(const stem_plan_info &in, PlanDev pd, const float *qbar,
                         const float *kbar, const float *vnorm, float *scores,
                         hipStream_t st);
+// Anti-diagonal sampled metric (antidiag.hip): block logits from the token
+// logits, then the metric in place; units_per_head bounds its tile pairs.
+int64_t antidiag_units_per_head(const stem_plan_info &in, int stride);
+hipError_t launch_score_antidiag(const stem_plan_info &in, PlanDev pd, const void *q,
+                                 const void *k, const float *vnorm, int stride,
+                                 float *scores, hipStream_t st);
 hipError_t launch_select(const stem_plan_info &in, PlanDev pd, const float *scores,
                          int32_t *idx, int32_t *count, hipStream_t st);
 hipError_t launch_attn(const stem_plan_info &in, PlanDev pd, const void *q,

@@ -93,6 +93,8 @@ _SIGS = {
                                  ctypes.c_int32, _P]),
     "stem_score": (ctypes.c_int, [ctypes.POINTER(stem_plan_info), _P, _P, _P, _P, _P, _P]),
     "stem_select": (ctypes.c_int, [ctypes.POINTER(stem_plan_info), _P, _P, _P, _P, _P]),
+    "stem_score_antidiag": (ctypes.c_int, [ctypes.POINTER(stem_plan_info), _P, _P, _P, _P,
+                                           ctypes.c_int32, _P, _P]),
     "stem_sparse_attn": (ctypes.c_int, [ctypes.POINTER(stem_plan_info), _P, _P, _P, _P, _P, _P,
                                         _P, ctypes.c_int32, _P, _P]),
     "stem_status_str": (ctypes.c_char_p, [ctypes.c_int]),
@@ -262,6 +264,19 @@ def stem_score(plan: Plan, qbar, kbar, vnorm, scores, stream=None) -> None:
                                           _stream(stream)))
 
 
+def stem_score_antidiag(plan: Plan, q, k, vnorm, stride: int, scores, stream=None) -> None:
+    import torch
+    i = plan.info
+    _need(q, "q", torch.bfloat16, (i.total_tokens, i.num_q_heads, i.head_dim))
+    _need(k, "k", torch.bfloat16, (i.total_tokens, i.num_kv_heads, i.head_dim))
+    _need(vnorm, "vnorm", torch.float32, (i.num_kv_heads, i.total_blocks))
+    _need(scores, "scores", torch.float32, (i.num_q_heads, i.score_elems_per_head))
+    _check("stem_score_antidiag",
+           lib().stem_score_antidiag(ctypes.byref(i), plan.dev_ptr, q.data_ptr(), k.data_ptr(),
+                                     vnorm.data_ptr(), int(stride), scores.data_ptr(),
+                                     _stream(stream)))
+
+
 def stem_select(plan: Plan, scores, idx, count, stream=None) -> None:
     import torch
     i = plan.info
@@ -347,12 +362,18 @@ class Buffers:
 
 
 def prefill(plan: Plan, q, k, v, bufs: Optional[Buffers] = None, out_dtype=None,
-            vnorm_mode: int = STEM_VNORM_MEAN, stream=None) -> Buffers:
-    """pool -> score -> select -> sparse attention, all on the GPU."""
+            vnorm_mode: int = STEM_VNORM_MEAN, stream=None,
+            score_stride: Optional[int] = None) -> Buffers:
+    """pool -> score -> select -> sparse attention, all on the GPU.  With
+    score_stride set, the metric comes from anti-diagonal samples of the
+    token logits (stem_score_antidiag) instead of the pooled blocks."""
     if bufs is None:
         bufs = Buffers(plan, q.device, out_dtype)
     stem_pool(plan, q, k, v, bufs.qbar, bufs.kbar, bufs.vnorm, vnorm_mode, stream)
-    stem_score(plan, bufs.qbar, bufs.kbar, bufs.vnorm, bufs.scores, stream)
+    if score_stride is None:
+        stem_score(plan, bufs.qbar, bufs.kbar, bufs.vnorm, bufs.scores, stream)
+    else:
+        stem_score_antidiag(plan, q, k, bufs.vnorm, score_stride, bufs.scores, stream)
     stem_select(plan, bufs.scores, bufs.idx, bufs.count, stream)
     stem_sparse_attn(plan, q, k, v, bufs.idx, bufs.count, bufs.out, bufs.lse, stream)
     return bufs

@@ -173,6 +173,26 @@ int stem_score(const stem_plan_info *info, const void *plan_dev,
                const float *qbar, const float *kbar, const float *vnorm,
                float *scores, void *stream);
 
+/* stem_score_antidiag - the metric of stem_score with block logits taken from
+ * anti-diagonal samples of the token logits instead of the pooled blocks
+ * (gist.science/fr, "Resume technique" 2.C step 1: block metrics computed
+ * with anti-diagonal sampling).  For stride S (a power of two, 1 <= S <= B),
+ * each sequence's tokens form groups of S positions; the sample of query
+ * group r and key group c is the mean of q.k / sqrt(d) over the pairs
+ * (query rS + S-1-u, key cS + u), u = 0..S-1, whose tokens exist and whose
+ * key is not after the query; the block logit t_ij is the log of the mean of
+ * exp(sample) over the samples of query block i and key block j (-inf if
+ * there are none) and takes the place of s_ij in the metric mode of the plan.
+ * A row whose logits are all -inf gets 0 in the softmax forms.  S = 1 gives
+ * the exact log-mean-exp of each block pair's causal token logits.
+ *   q [T, Hq, d], k [T, Hkv, d]: bf16 only (STEM_EUNSUPPORTED for f32 plans),
+ *   16-byte aligned; vnorm [Hkv, nbT] f32 from stem_pool; scores as for
+ *   stem_score (fully overwritten).  STEM_EINVAL for a bad stride; the
+ *   work bound Hq * tile pairs must stay below 2^30 (STEM_EUNSUPPORTED). */
+int stem_score_antidiag(const stem_plan_info *info, const void *plan_dev,
+                        const void *q, const void *k, const float *vnorm, int32_t stride,
+                        float *scores, void *stream);
+
 /* stem_select - Token Position-Decay top-k (gist.science/es
  * "Implementacion" steps 2-3, gist.science/nl "Implementatie" steps 2-3).
  * For each (query head, query block i): the sinks {0 .. min(S, i+1) - 1}

@@ -40,14 +40,16 @@ class GpuRun:
     """Plan, upload and run the whole path once; keep host copies."""
 
     def __init__(self, w: syn.Workload, x: syn.Inputs = None, out_dtype="f32", vnorm_mode=0,
-                 plan_override=None):
+                 plan_override=None, score_stride=None):
         import torch
         self.w = w
         self.x = x if x is not None else syn.generate(w)
         self.plan = stem.plan_for(w, **(plan_override or {})).to("cuda")
         q, k, v = upload(self.x)
         odt = torch.float32 if out_dtype == "f32" else torch.bfloat16
-        b = stem.prefill(self.plan, q, k, v, out_dtype=odt, vnorm_mode=vnorm_mode)
+        b = stem.prefill(self.plan, q, k, v, out_dtype=odt, vnorm_mode=vnorm_mode,
+                         score_stride=score_stride)
+        self.score_stride = score_stride
         torch.cuda.synchronize()
         self.qbar = b.qbar.cpu().numpy()
         self.kbar = b.kbar.cpu().numpy()

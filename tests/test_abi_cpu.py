@@ -193,3 +193,23 @@ def test_device_calls_reject_bad_arguments_before_any_launch():
         assert L.stem_sparse_attn(ctypes.byref(big), P, P, P, P, P, P, P, 0, None, None) == \
             stem.STEM_EUNSUPPORTED, field
     assert stem.status_str(stem.STEM_EUNSUPPORTED) == "unsupported configuration"
+
+
+def test_antidiag_score_rejects_bad_arguments_before_any_launch():
+    L = stem.lib()
+    P = 1 << 20
+    info = stem.plan_for(syn.custom([256], 4, 2, 64, "bf16", 64)).info
+    A = L.stem_score_antidiag
+    for stride in (0, -1, 3, 6, 128, 1 << 20):
+        assert A(ctypes.byref(info), P, P, P, P, stride, P, None) == stem.STEM_EINVAL, stride
+    assert A(ctypes.byref(info), P, None, P, P, 4, P, None) == stem.STEM_EINVAL
+    assert A(ctypes.byref(info), P, P + 8, P, P, 4, P, None) == stem.STEM_EINVAL
+    assert A(ctypes.byref(info), P, P, P, P + 2, 4, P, None) == stem.STEM_EINVAL
+    f32 = stem.plan_for(syn.custom([256], 4, 2, 64, "f32", 64)).info
+    assert A(ctypes.byref(f32), P, P, P, P, 4, P, None) == stem.STEM_EUNSUPPORTED
+    # stride 1 on the longest sequence with many heads exceeds the work bound
+    big = stem.plan_for(syn.custom([64 * 4096], 1024, 1, 64, "bf16", 64)).info
+    assert A(ctypes.byref(big), P, P, P, P, 1, P, None) == stem.STEM_EUNSUPPORTED
+    # an empty problem is accepted without a launch
+    empty = stem.plan_for(syn.custom([0], 4, 2, 64, "bf16", 64)).info
+    assert A(ctypes.byref(empty), None, None, None, None, 4, None, None) == stem.STEM_OK
