@@ -13,22 +13,26 @@
 // Kernel 1 (antidiag_kernel): the samples are a causal matrix product per
 // query head, Q' K'^T / S, where row r of Q' is the concatenation of the
 // query tokens rS + S-1, rS + S-2, ..., rS of that head and row c of K' the
-// key tokens cS, ..., cS + S-1 (depth S d).  One workgroup computes one
-// 128 x 128 tile of groups with bf16 matrix cores (v_mfma_f32_32x32x16_bf16,
-// f32 accumulation): 4 wavefronts of 64 x 64, operands staged through LDS
-// 64 dimensions of one token position u at a time (16 KiB per operand per
-// stage, double buffered, the next stage's global loads in flight while the
-// current one is multiplied).  Block pairs never straddle a tile (128 groups
-// are a whole number of blocks), so the tile finishes its block logits
-// itself: samples go to LDS, a first pass reduces each (group row, key
-// block) segment to a max and a sum of exponentials, a second pass combines
-// the rows of each query block.
+// key tokens cS, ..., cS + S-1 (depth S d).  One workgroup of 4 wavefronts
+// computes a tile of 256 query groups x 128 key groups on the bf16 matrix
+// cores (v_mfma_f32_32x32x16_bf16, f32 accumulation), each wavefront 64 rows
+// x 128 columns (eight 32 x 32 products: 6 KiB of LDS operand reads per 8
+// products).  Operands arrive by global->LDS DMA, 32 dimensions of one token
+// position u per stage (24 KiB), three stages in flight; two workgroups share
+// a CU, so one's epilogue overlaps the other's products.  Block pairs never
+// straddle a tile (its sides are whole numbers of blocks), so the tile
+// finishes its block logits itself, in registers: within each 32 x 32
+// product the samples of a block pair (or of its 32 x 32 part, combined
+// through LDS when blocks hold more than 32 groups) are reduced to a max and
+// a sum of exponentials by in-lane steps and cross-lane shuffles.
 //
-// Only the diagonal tile of each row of tiles holds samples whose
-// anti-diagonal crosses the causal boundary (r = c): there the pairs with
-// u >= ceil(S/2) have the key after the query, so those entries are frozen
-// once the products of u < ceil(S/2) are accumulated.  Tokens past the end of
-// a sequence load as zeros; each sample is divided by its own pair count.
+// Only the tiles on the diagonal hold samples whose anti-diagonal crosses the
+// causal boundary (r = c): there the pairs with u >= ceil(S/2) have the key
+// after the query, so those entries are frozen once the products of
+// u < ceil(S/2) are accumulated.  Token rows past the end of a sequence are
+// clamped to its last token and their samples masked; in the tiles holding a
+// short last group, the staged rows of its missing tokens are zeroed, so each
+// sample sums exactly its own pairs and is divided by its own pair count.
 //
 // Kernel 2 (antidiag_metric_kernel): one wavefront per metric row turns the
 // row's block logits into the metric in place (row softmax times V magnitude,
@@ -38,9 +42,15 @@
 namespace stem {
 namespace {
 
-constexpr int kTile = 128;             // groups per tile side
-constexpr int kRowBytes = 128;         // one staged row: 64 bf16 dimensions
-constexpr int kOpBytes = kTile * kRowBytes;   // 16 KiB per operand per stage
+constexpr int kTM = 256;                 // query groups per tile
+constexpr int kTN = 128;                 // key groups per tile
+constexpr int kSRow = 64;                // bytes per staged row: 32 bf16 dimensions
+constexpr int kAB = kTM * kSRow;         // 16 KiB of Q' per stage
+constexpr int kStage = kAB + kTN * kSRow;   // + 8 KiB of K'
+constexpr int kNBuf = 3;
+constexpr int kDmaA = kAB / 1024 / 4;    // 1 KiB DMAs per wavefront per stage: 4 for Q'
+constexpr int kDmaB = kTN * kSRow / 1024 / 4;   // and 2 for K'
+constexpr float kLog2e = 1.4426950408889634f;
 
 struct AdArgs {
   const char *q, *k;
@@ -52,26 +62,27 @@ struct AdArgs {
   float scale;                // 1 / sqrt(d)
 };
 
-// Locate tile pair u of the head's work: sequence s, row tile rt, column tile
-// ct.  Pairs are numbered per sequence in bands of two row tiles, column tile
-// major inside a band, so that work in flight together shares both operands.
+// Tile pairs of a sequence with ng groups: row tile rt pairs with column
+// tiles 0 .. min(2 rt + 1, ntc - 1), so rt(rt + 1) pairs precede row tile rt.
+__device__ __forceinline__ int seq_pairs(int ng) {
+  const int ntr = (ng + kTM - 1) / kTM, ntc = (ng + kTN - 1) / kTN;
+  return ntr * (ntr + 1) - (2 * ntr - ntc);
+}
+
+// Locate tile pair u of the head's work (sequence s, row tile rt, column
+// tile ct); column tiles are innermost, so work in flight together shares
+// its row tile of Q'.
 __device__ __forceinline__ bool decode_unit(const AdArgs &a, int u, int &s, int &rt, int &ct) {
   for (s = 0; s < a.num_seqs; ++s) {
     const int len = a.pd.cu_seqlens[s + 1] - a.pd.cu_seqlens[s];
-    const int ng = (len + a.stride - 1) / a.stride;
-    const int nt = (ng + kTile - 1) / kTile;
-    const int pairs = nt * (nt + 1) / 2;
+    const int pairs = seq_pairs((len + a.stride - 1) / a.stride);
     if (u >= pairs) { u -= pairs; continue; }
-    for (int b = 0;; ++b) {
-      const int r0 = 2 * b;
-      const bool two = r0 + 1 < nt;
-      const int cnt = two ? 2 * (r0 + 1) + 1 : r0 + 1;
-      if (u >= cnt) { u -= cnt; continue; }
-      if (!two) { rt = r0; ct = u; }
-      else if (u < 2 * (r0 + 1)) { ct = u >> 1; rt = r0 + (u & 1); }
-      else { ct = r0 + 1; rt = r0 + 1; }
-      return true;
-    }
+    int x = int((sqrtf(4.0f * float(u) + 1.0f) - 1.0f) * 0.5f);
+    while (x * (x + 1) > u) --x;
+    while ((x + 1) * (x + 2) <= u) ++x;
+    rt = x;
+    ct = u - x * (x + 1);
+    return true;
   }
   return false;
 }
@@ -85,10 +96,72 @@ __device__ __forceinline__ int pair_count(int r, int c, int S, int len) {
   return max(0, min(m - 1, half - 1) - (S - m) + 1);
 }
 
+// Samples of block pair (i, j) of a sequence with ng groups (gpb groups per
+// block): every column of block j for each of block i's rows when j < i; the
+// causal triangle plus the diagonal samples that hold a pair when j == i.
+__device__ __forceinline__ int pair_samples(int i, int j, int gpb, int ng, int S, int len) {
+  const int rows = min(gpb, ng - i * gpb);
+  if (j < i) return rows * gpb;
+  int ns = rows * (rows - 1) / 2;
+  for (int x = 0; x < rows; ++x) ns += pair_count(i * gpb + x, i * gpb + x, S, len) > 0;
+  return ns;
+}
+
+__device__ __forceinline__ float shfl_max(float v, int o) { return fmaxf(v, __shfl_xor(v, o)); }
+__device__ __forceinline__ float shfl_add(float v, int o) { return v + __shfl_xor(v, o); }
+
+// Max and sum of exp(x - max) over groups of G x G samples of one 32 x 32
+// product (G = 1 .. 32), G consecutive rows by G consecutive columns.  Lane
+// (n, hi) holds rows 8 (e / 4) + 4 hi + e % 4 of column n, e = 0..15.  On
+// return mx[k], sm[k] hold the result of the lane's k-th row group (k < NR)
+// in every lane of the group's columns (and both halves when G >= 8).
+template <int G>
+struct Groups {
+  static constexpr int EG = G <= 4 ? G : (G == 8 ? 4 : (G == 16 ? 8 : 16));   // elements per in-lane group
+  static constexpr int NR = 16 / EG;
+  __device__ __forceinline__ static void reduce(const float (&x)[16], float (&mx)[NR], float (&sm)[NR]) {
+#pragma unroll
+    for (int k = 0; k < NR; ++k) {
+      float v = x[k * EG];
+#pragma unroll
+      for (int e = 1; e < EG; ++e) v = fmaxf(v, x[k * EG + e]);
+      if constexpr (G >= 8) v = shfl_max(v, 32);
+#pragma unroll
+      for (int o = 1; o < G; o <<= 1) v = shfl_max(v, o);
+      mx[k] = v;
+    }
+#pragma unroll
+    for (int k = 0; k < NR; ++k) {
+      float v = 0.f;
+      if (mx[k] != -INFINITY) {
+#pragma unroll
+        for (int e = 0; e < EG; ++e) v += exp2f((x[k * EG + e] - mx[k]) * kLog2e);
+      }
+      if constexpr (G >= 8) v = shfl_add(v, 32);
+#pragma unroll
+      for (int o = 1; o < G; o <<= 1) v = shfl_add(v, o);
+      sm[k] = v;
+    }
+  }
+  // first row (within the 32 x 32 product) of the lane's k-th row group
+  __device__ __forceinline__ static int row_of(int k, int hi) {
+    const int e = k * EG;
+    return 8 * (e >> 2) + (G >= 8 ? 0 : 4 * hi) + (e & 3);
+  }
+};
+
+// Group size of the epilogue, and whether a group is a whole block pair
+// (blocks of at most 32 groups) or a 32 x 32 part of one.
+template <int G, bool WHOLE>
+struct GroupTag {
+  static constexpr int kG = G;
+  static constexpr bool kWhole = WHOLE;
+};
+
 template <int D>
-__global__ __launch_bounds__(256) void antidiag_kernel(AdArgs a) {
-  constexpr int HALVES = D / 64;
-  __shared__ __attribute__((aligned(16))) char lds[2 * 2 * kOpBytes];
+__global__ __launch_bounds__(256, 2) void antidiag_kernel(AdArgs a) {
+  constexpr int QTR = D / 32;              // 32-dimension stages per token position
+  __shared__ __attribute__((aligned(16))) char lds[kNBuf * kStage];
 
   // XCD-aware numbering: consecutive workgroup ids go round robin over the 8
   // XCDs, so each XCD receives a contiguous range of units (grid % 8 == 0)
@@ -104,169 +177,235 @@ __global__ __launch_bounds__(256) void antidiag_kernel(AdArgs a) {
   const int t0 = a.pd.cu_seqlens[s];
   const int len = a.pd.cu_seqlens[s + 1] - t0;
   const int ng = (len + S - 1) / S;
-  const int r0 = rt * kTile, c0 = ct * kTile;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int r0 = rt * kTM, c0 = ct * kTN;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hi = lane >> 5, n32 = lane & 31;
+  const int nst = S * QTR;
 
-  // ---- staging roles: thread loads rows lrow + 32 p (p = 0..3), 16-byte chunk lch
-  const int lrow = tid >> 3, lch = tid & 7;
+  // ---- DMA roles: DMA k of a stage moves 16 staged rows (1 KiB); lane L
+  // lands at row 16 k + L / 4, LDS chunk L % 4, which holds the row's logical
+  // chunk (L % 4) ^ ((row >> 1) & 3): the operand reads below are free of
+  // bank conflicts
   const int64_t qrow = int64_t(a.Hq) * D * 2, krow = int64_t(a.Hkv) * D * 2;
-  const uint32_t st_off = uint32_t(lrow * kRowBytes + ((lch ^ (lrow & 7)) << 4));
-  const int nst = S * HALVES;
-
-  u32x4 ra[4], rb[4];
-  auto load = [&](int st) {
-    const int u = st / HALVES, half = st % HALVES;
+  const int drow = lane >> 2;
+  const char *qtile = a.q + (int64_t(t0) + int64_t(r0) * S) * qrow + int64_t(h) * D * 2;
+  const char *ktile = a.k + (int64_t(t0) + int64_t(c0) * S) * krow + int64_t(hk) * D * 2;
+  const int qlim = len - 1 - r0 * S, klim = len - 1 - c0 * S;   // last token, tile-relative
+  const uint32_t lds0 = lds_addr_of(lds);
+  auto issue = [&](int st, int buf) {
+    const int u = st / QTR, qt = st - u * QTR;
+    const uint32_t sb = lds0 + buf * kStage;
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      const int qp = (r0 + lrow + 32 * p) * S + S - 1 - u;
-      const int kp = (c0 + lrow + 32 * p) * S + u;
-      const char *qa = a.q + (int64_t(t0) + qp) * qrow + int64_t(h) * D * 2 + half * 128 + lch * 16;
-      const char *ka = a.k + (int64_t(t0) + kp) * krow + int64_t(hk) * D * 2 + half * 128 + lch * 16;
-      ra[p] = qp < len ? *reinterpret_cast<const u32x4 *>(qa) : u32x4{0u, 0u, 0u, 0u};
-      rb[p] = kp < len ? *reinterpret_cast<const u32x4 *>(ka) : u32x4{0u, 0u, 0u, 0u};
+    for (int x = 0; x < kDmaA; ++x) {
+      const int row = 16 * (w + 4 * x) + drow;
+      const int chunk = (lane & 3) ^ ((row >> 1) & 3);
+      const int tok = min(row * S + S - 1 - u, qlim);
+      dma16(qtile + qt * 64, uint32_t(tok) * uint32_t(qrow) + chunk * 16, sb + (w + 4 * x) * 1024);
+    }
+#pragma unroll
+    for (int x = 0; x < kDmaB; ++x) {
+      const int row = 16 * (w + 4 * x) + drow;
+      const int chunk = (lane & 3) ^ ((row >> 1) & 3);
+      const int tok = min(row * S + u, klim);
+      dma16(ktile + qt * 64, uint32_t(tok) * uint32_t(krow) + chunk * 16,
+            sb + kAB + (w + 4 * x) * 1024);
     }
   };
-  auto store = [&](int buf) {
-    char *A = lds + buf * 2 * kOpBytes, *Bm = A + kOpBytes;
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      *reinterpret_cast<u32x4 *>(A + st_off + p * 32 * kRowBytes) = ra[p];
-      *reinterpret_cast<u32x4 *>(Bm + st_off + p * 32 * kRowBytes) = rb[p];
-    }
-  };
 
-  // ---- products: wavefront (wr, wc) owns rows wr*64.. and columns wc*64..
-  const int wr = w >> 1, wc = w & 1;
-  f32x16 acc[2][2];
+  // a short last group in this tile: its missing tokens' staged rows are
+  // zeroed after they land (query row r_last for u < S - m, key row c_last
+  // for u >= m, m = tokens in the last group)
+  const int m_last = len - (ng - 1) * S;
+  const bool partial = m_last < S && ((ng - 1 >= r0 && ng - 1 < r0 + kTM) ||
+                                      (ng - 1 >= c0 && ng - 1 < c0 + kTN));
+
+  // ---- products: wavefront w owns rows 64 w .. 64 w + 63, all 128 columns
+  f32x16 acc[2][4];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
+  // rows wholly above the causal boundary or past the sequence: no products
+  const bool idle = r0 + 64 * w + 63 < c0 || r0 + 64 * w >= ng;
   auto compute = [&](int buf) {
-    const char *A = lds + buf * 2 * kOpBytes, *Bm = A + kOpBytes;
+    const char *A = lds + buf * kStage, *Bm = A + kAB;
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      const int chunk = ((2 * kk + hi) ^ (n32 & 7)) << 4;
-      bf16x8 af[2], bfr[2];
-#pragma unroll
-      for (int m = 0; m < 2; ++m)
-        af[m] = *reinterpret_cast<const bf16x8 *>(A + (wr * 64 + m * 32 + n32) * kRowBytes + chunk);
-#pragma unroll
-      for (int n = 0; n < 2; ++n)
-        bfr[n] = *reinterpret_cast<const bf16x8 *>(Bm + (wc * 64 + n * 32 + n32) * kRowBytes + chunk);
+    for (int kk = 0; kk < 2; ++kk) {
+      const int chunk = ((2 * kk + hi) ^ ((n32 >> 1) & 3)) << 4;
+      bf16x8 af[2], bfr[4];
 #pragma unroll
       for (int m = 0; m < 2; ++m)
+        af[m] = *reinterpret_cast<const bf16x8 *>(A + (64 * w + 32 * m + n32) * kSRow + chunk);
 #pragma unroll
-        for (int n = 0; n < 2; ++n)
+      for (int n = 0; n < 4; ++n)
+        bfr[n] = *reinterpret_cast<const bf16x8 *>(Bm + (32 * n + n32) * kSRow + chunk);
+#pragma unroll
+      for (int m = 0; m < 2; ++m)
+#pragma unroll
+        for (int n = 0; n < 4; ++n)
           acc[m][n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[m], bfr[n], acc[m][n], 0, 0, 0);
     }
   };
 
-  // diagonal entries (row == column) of the diagonal 32 x 32 products: lane
-  // (n32, hi) holds the one at element e_diag, if any
-  const bool diag_wave = rt == ct && wr == wc;
+  // diagonal entries (r == c): product (m, ndg + m) of this wavefront, lane
+  // (n32, hi) holding the one at element e_diag if any
+  const int ndg = 2 * w - 4 * (ct - 2 * rt);
+  const bool diag_wave = ndg > -2 && ndg < 4;
   const int xd = n32 - 4 * hi;
   const bool has_diag = xd >= 0 && (xd & 4) == 0;
   const int e_diag = ((xd >> 3) << 2) | (xd & 3);
-  const int st_freeze = ((S + 1) >> 1) * HALVES - 1;
+  const int st_freeze = ((S + 1) >> 1) * QTR - 1;
   float frozen[2] = {0.f, 0.f};
 
-  load(0);
-  store(0);
-  __syncthreads();
+  issue(0, 0);
+  issue(1, 1);                             // nst >= 2 (S >= 1, D >= 64)
   for (int st = 0; st < nst; ++st) {
-    if (st + 1 < nst) load(st + 1);
-    compute(st & 1);
+    if (st + 1 < nst) __builtin_amdgcn_s_waitcnt(0x0F70 | (kDmaA + kDmaB));
+    else wait_vm();
+    __syncthreads();
+    const int buf = st % kNBuf;
+    if (partial) {
+      const int u = st / QTR;
+      char *A = lds + buf * kStage;
+      if (tid < 4 && u < S - m_last && ng - 1 >= r0 && ng - 1 < r0 + kTM)
+        *reinterpret_cast<u32x4 *>(A + (ng - 1 - r0) * kSRow + tid * 16) = u32x4{0u, 0u, 0u, 0u};
+      if (tid >= 4 && tid < 8 && u >= m_last && ng - 1 >= c0 && ng - 1 < c0 + kTN)
+        *reinterpret_cast<u32x4 *>(A + kAB + (ng - 1 - c0) * kSRow + (tid - 4) * 16) =
+            u32x4{0u, 0u, 0u, 0u};
+      wait_lgkm();
+      __syncthreads();
+    }
+    if (st + 2 < nst) issue(st + 2, (st + 2) % kNBuf);
+    if (!idle) compute(buf);
     if (diag_wave && st == st_freeze) {
 #pragma unroll
       for (int m = 0; m < 2; ++m)
 #pragma unroll
-        for (int e = 0; e < 16; ++e)
-          if (e == e_diag) frozen[m] = acc[m][m][e];
+        for (int n = 0; n < 4; ++n)
+          if (n == ndg + m)
+#pragma unroll
+            for (int e = 0; e < 16; ++e)
+              if (e == e_diag) frozen[m] = acc[m][n][e];
     }
-    if (st + 1 < nst) store((st + 1) & 1);
-    __syncthreads();
   }
   if (diag_wave && has_diag) {
 #pragma unroll
     for (int m = 0; m < 2; ++m)
 #pragma unroll
-      for (int e = 0; e < 16; ++e)
-        if (e == e_diag) acc[m][m][e] = frozen[m];
+      for (int n = 0; n < 4; ++n)
+        if (n == ndg + m)
+#pragma unroll
+          for (int e = 0; e < 16; ++e)
+            if (e == e_diag) acc[m][n][e] = frozen[m];
   }
 
-  // ---- samples to LDS: f32 [128][128], -inf where there is no sample
-  float *smp = reinterpret_cast<float *>(lds);
-#pragma unroll
-  for (int m = 0; m < 2; ++m)
-#pragma unroll
-    for (int n = 0; n < 2; ++n)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int rl = wr * 64 + m * 32 + 8 * (e >> 2) + 4 * hi + (e & 3);
-        const int cl = wc * 64 + n * 32 + n32;
-        const int r = r0 + rl, c = c0 + cl;
-        const int cnt = (r < ng && c <= r) ? pair_count(r, c, S, len) : 0;
-        smp[rl * kTile + cl] = cnt > 0 ? acc[m][n][e] * (a.scale / float(cnt)) : -INFINITY;
-      }
-  __syncthreads();
-
-  // ---- pass 1: each (row, key block) segment -> max and sum of exp(x - max),
-  // left in the segment's first two slots
-  const int gpb = a.block / S;             // groups per block
-  const int nbt = kTile / max(gpb, 1);     // blocks per tile side (gpb <= 128)
-  constexpr float kLog2e = 1.4426950408889634f;
-  if (gpb > 1) {
-    for (int it = tid; it < kTile * nbt; it += 256) {
-      const int rl = it / nbt, jb = it - rl * nbt;
-      float *seg = smp + rl * kTile + jb * gpb;
-      float mx = -INFINITY;
-      for (int x = 0; x < gpb; ++x) mx = fmaxf(mx, seg[x]);
-      float sum = 0.f;
-      if (mx != -INFINITY)
-        for (int x = 0; x < gpb; ++x) sum += exp2f((seg[x] - mx) * kLog2e);
-      seg[0] = mx;
-      seg[1] = sum;
-    }
-    __syncthreads();
-  }
-
-  // ---- pass 2: combine the rows of each query block; write t_ij
-  const int nrow_g = ng - r0;              // valid group rows in this tile (> 0)
-  const int b_r0 = r0 / gpb, b_c0 = c0 / gpb;
+  // ---- block logits
+  const int gpb = a.block / S;             // groups per block (1 .. 128)
   const int nb = a.pd.cu_blocks[s + 1] - a.pd.cu_blocks[s];
   float *orow = a.out + int64_t(h) * a.per_head + a.pd.tri[s];
-  for (int it = tid; it < nbt * nbt; it += 256) {
-    const int ib = it / nbt, jb = it - ib * nbt;
-    const int i = b_r0 + ib, j = b_c0 + jb;
-    if (i >= nb || j > i) continue;
-    float mx = -INFINITY;
-    const int rows = min(gpb, nrow_g - ib * gpb);
-    for (int x = 0; x < rows; ++x) mx = fmaxf(mx, smp[(ib * gpb + x) * kTile + jb * gpb]);
-    float t = -INFINITY;
-    if (mx != -INFINITY) {
-      float sum = 0.f;
-      for (int x = 0; x < rows; ++x) {
-        const float *seg = smp + (ib * gpb + x) * kTile + jb * gpb;
-        const float l = gpb > 1 ? seg[1] : (seg[0] != -INFINITY ? 1.f : 0.f);
-        if (seg[0] != -INFINITY) sum += l * exp2f((seg[0] - mx) * kLog2e);
+  // every sample of the tile exists and counts S pairs: all key groups before
+  // all query groups, all query groups full
+  const bool interior = c0 + kTN <= r0 && (r0 + kTM) * S <= len;
+  const float fscale = a.scale / float(S);
+
+  auto finish = [&](auto grp) __attribute__((always_inline)) {
+    using Gr = decltype(grp);
+    constexpr int G = Gr::kG;
+    using R = Groups<G>;
+    // one 32 x 32 product at a time (a loop, not unrolled: the code stays
+    // small; the product is first copied out with constant indices)
+#pragma unroll 1
+    for (int t = 0; t < 8; ++t) {
+      const int m = t >> 2, n = t & 3;
+      float x[16];
+      switch (t) {
+#define STEM_AD_TAKE(T)                                              \
+  case T:                                                            \
+    _Pragma("unroll") for (int e = 0; e < 16; ++e) x[e] = acc[T >> 2][T & 3][e]; \
+    break;
+        STEM_AD_TAKE(0) STEM_AD_TAKE(1) STEM_AD_TAKE(2) STEM_AD_TAKE(3)
+        STEM_AD_TAKE(4) STEM_AD_TAKE(5) STEM_AD_TAKE(6) STEM_AD_TAKE(7)
+#undef STEM_AD_TAKE
       }
-      // samples of the pair: every column of block j for each row when
-      // j < i; the causal triangle plus the diagonal samples when j == i
-      int ns;
-      if (j < i) {
-        ns = rows * gpb;
+      const int rb = r0 + 64 * w + 32 * m, cb = c0 + 32 * n;
+      if (idle) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) x[e] = -INFINITY;
+      } else if (interior) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) x[e] *= fscale;
       } else {
-        ns = rows * (rows - 1) / 2;
-        for (int x = 0; x < rows; ++x) {
-          const int r = r0 + ib * gpb + x;
-          ns += pair_count(r, r, S, len) > 0;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int r = rb + 8 * (e >> 2) + 4 * hi + (e & 3), c = cb + n32;
+          const int cnt = (r < ng && c <= r) ? pair_count(r, c, S, len) : 0;
+          x[e] = cnt > 0 ? x[e] * (a.scale / float(cnt)) : -INFINITY;
         }
       }
-      t = mx + __logf(sum / float(ns));
+      float mx[R::NR], sm[R::NR];
+      R::reduce(x, mx, sm);
+      if constexpr (G < 32 || Gr::kWhole) {
+        // whole block pairs: lanes at the first column of a group write
+        if (n32 % G == 0 && (G < 8 || hi == 0)) {
+#pragma unroll
+          for (int k = 0; k < R::NR; ++k) {
+            const int i = (rb + R::row_of(k, hi)) / G, j = (cb + n32) / G;
+            if (i < nb && j <= i) {
+              float tv = -INFINITY;
+              if (mx[k] != -INFINITY) {
+                const int ns = interior ? G * G : pair_samples(i, j, G, ng, S, len);
+                tv = mx[k] + __logf(sm[k] / float(ns));
+              }
+              orow[int64_t(i) * (i + 1) / 2 + j] = tv;
+            }
+          }
+        }
+      } else {
+        // blocks of more than 32 groups: partial results of this 32 x 32
+        // product, combined below
+        if (lane == 0) {
+          f32x2 *part = reinterpret_cast<f32x2 *>(lds);
+          part[(2 * w + m) * 4 + n] = f32x2{mx[0], sm[0]};
+        }
+      }
     }
-    orow[int64_t(i) * (i + 1) / 2 + j] = t;
+  };
+  switch (gpb) {
+    case 1: finish(GroupTag<1, true>{}); return;
+    case 2: finish(GroupTag<2, true>{}); return;
+    case 4: finish(GroupTag<4, true>{}); return;
+    case 8: finish(GroupTag<8, true>{}); return;
+    case 16: finish(GroupTag<16, true>{}); return;
+    case 32: finish(GroupTag<32, true>{}); return;
+    default: break;
+  }
+  // gpb = 64 or 128: 32 x 32 partials through LDS (the staging area is free
+  // once every wavefront has passed this barrier)
+  __syncthreads();
+  finish(GroupTag<32, false>{});
+  __syncthreads();
+  const f32x2 *part = reinterpret_cast<const f32x2 *>(lds);
+  const int pr = kTM / gpb, pc = kTN / gpb, per = gpb / 32;
+  if (tid < pr * pc) {
+    const int ib = tid / pc, jb = tid - ib * pc;
+    const int i = r0 / gpb + ib, j = c0 / gpb + jb;
+    if (i < nb && j <= i) {
+      float mx = -INFINITY;
+      for (int x = 0; x < per; ++x)
+        for (int y = 0; y < per; ++y) mx = fmaxf(mx, part[(ib * per + x) * 4 + jb * per + y][0]);
+      float t = -INFINITY;
+      if (mx != -INFINITY) {
+        float sum = 0.f;
+        for (int x = 0; x < per; ++x)
+          for (int y = 0; y < per; ++y) {
+            const f32x2 pv = part[(ib * per + x) * 4 + jb * per + y];
+            if (pv[0] != -INFINITY) sum += pv[1] * exp2f((pv[0] - mx) * kLog2e);
+          }
+        t = mx + __logf(sum / float(pair_samples(i, j, gpb, ng, S, len)));
+      }
+      orow[int64_t(i) * (i + 1) / 2 + j] = t;
+    }
   }
 }
 
@@ -329,10 +468,11 @@ __global__ __launch_bounds__(256) void antidiag_metric_kernel(MetricArgs a) {
 }  // namespace
 
 int64_t antidiag_units_per_head(const stem_plan_info &in, int stride) {
+  // per sequence ntr (ntr + 1) pairs at most, ntr = row tiles of 256 groups
   const int64_t gpb = in.block / stride;
-  const int64_t ntmax = (int64_t(in.max_seq_blocks) * gpb + kTile - 1) / kTile;
-  const int64_t nt_sum = (in.total_blocks * gpb + kTile - 1) / kTile + in.num_seqs;
-  return (ntmax + 1) * nt_sum / 2 + 1;
+  const int64_t ntr_max = (int64_t(in.max_seq_blocks) * gpb + kTM - 1) / kTM;
+  const int64_t ntr_sum = (in.total_blocks * gpb + kTM - 1) / kTM + in.num_seqs;
+  return (ntr_max + 1) * ntr_sum + 1;
 }
 
 hipError_t launch_score_antidiag(const stem_plan_info &in, PlanDev pd, const void *q,

@@ -187,8 +187,9 @@ int stem_score(const stem_plan_info *info, const void *plan_dev,
  * the exact log-mean-exp of each block pair's causal token logits.
  *   q [T, Hq, d], k [T, Hkv, d]: bf16 only (STEM_EUNSUPPORTED for f32 plans),
  *   16-byte aligned; vnorm [Hkv, nbT] f32 from stem_pool; scores as for
- *   stem_score (fully overwritten).  STEM_EINVAL for a bad stride; the
- *   work bound Hq * tile pairs must stay below 2^30 (STEM_EUNSUPPORTED). */
+ *   stem_score (fully overwritten).  STEM_EINVAL for a bad stride;
+ *   STEM_EUNSUPPORTED when the work bound Hq * tile pairs reaches 2^30 or
+ *   256 * stride token rows of Q span 4 GiB. */
 int stem_score_antidiag(const stem_plan_info *info, const void *plan_dev,
                         const void *q, const void *k, const float *vnorm, int32_t stride,
                         float *scores, void *stream);
