@@ -51,6 +51,7 @@ constexpr int kNBuf = 3;
 constexpr int kDmaA = kAB / 1024 / 4;    // 1 KiB DMAs per wavefront per stage: 4 for Q'
 constexpr int kDmaB = kTN * kSRow / 1024 / 4;   // and 2 for K'
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
 
 struct AdArgs {
   const char *q, *k;
@@ -107,48 +108,71 @@ __device__ __forceinline__ int pair_samples(int i, int j, int gpb, int ng, int S
   return ns;
 }
 
-__device__ __forceinline__ float shfl_max(float v, int o) { return fmaxf(v, __shfl_xor(v, o)); }
-__device__ __forceinline__ float shfl_add(float v, int o) { return v + __shfl_xor(v, o); }
+// Data-parallel-primitive (DPP) move of x within rows of 16 lanes.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL,
+                                                               0xF, 0xF, false));
+}
+// op(x[l], x[l ^ 32]) in every lane l (only blocks of 32 or more groups
+// need it)
+template <bool MAX>
+__device__ __forceinline__ float halves(float x) {
+  const float y = __shfl_xor(x, 32);
+  return MAX ? fmaxf(x, y) : x + y;
+}
 
-// Max and sum of exp(x - max) over groups of G x G samples of one 32 x 32
-// product (G = 1 .. 32), G consecutive rows by G consecutive columns.  Lane
-// (n, hi) holds rows 8 (e / 4) + 4 hi + e % 4 of column n, e = 0..15.  On
-// return mx[k], sm[k] hold the result of the lane's k-th row group (k < NR)
-// in every lane of the group's columns (and both halves when G >= 8).
+// Combine x over groups of G consecutive lanes (G = 1 .. 32) within each
+// half of the wavefront: butterflies of quad permutes and row mirrors.
+template <int G, bool MAX>
+__device__ __forceinline__ float lane_reduce(float x) {
+  auto op = [](float a, float b) { return MAX ? fmaxf(a, b) : a + b; };
+  if constexpr (G >= 2) x = op(x, dpp<0xB1>(x));     // quad_perm [1,0,3,2]
+  if constexpr (G >= 4) x = op(x, dpp<0x4E>(x));     // quad_perm [2,3,0,1]
+  if constexpr (G >= 8) x = op(x, dpp<0x141>(x));    // row_half_mirror
+  if constexpr (G >= 16) x = op(x, dpp<0x140>(x));   // row_mirror
+  if constexpr (G >= 32) x = op(x, __shfl_xor(x, 16));
+  return x;
+}
+
+// Max and sum of exp2(y - max) over groups of G x G samples of one 32 x 32
+// product (G = 1 .. 32).  The products' rows are permuted (see the operand
+// reads) so that lane (n, hi) holds rows 16 hi + e, e = 0..15, of column n:
+// a group's G rows (G <= 16) lie in one lane, its G columns in G consecutive
+// lanes.  On return mx[k], sm[k] hold the result of the lane's k-th row
+// group (k < NR) in every lane of the group's columns (and, for G = 32, of
+// both halves).
 template <int G>
 struct Groups {
-  static constexpr int EG = G <= 4 ? G : (G == 8 ? 4 : (G == 16 ? 8 : 16));   // elements per in-lane group
+  static constexpr int EG = G < 16 ? G : 16;   // elements of a group in one lane
   static constexpr int NR = 16 / EG;
-  __device__ __forceinline__ static void reduce(const float (&x)[16], float (&mx)[NR], float (&sm)[NR]) {
+  __device__ __forceinline__ static void reduce(const float (&y)[16], float (&mx)[NR], float (&sm)[NR]) {
 #pragma unroll
     for (int k = 0; k < NR; ++k) {
-      float v = x[k * EG];
+      float v = y[k * EG];
 #pragma unroll
-      for (int e = 1; e < EG; ++e) v = fmaxf(v, x[k * EG + e]);
-      if constexpr (G >= 8) v = shfl_max(v, 32);
-#pragma unroll
-      for (int o = 1; o < G; o <<= 1) v = shfl_max(v, o);
-      mx[k] = v;
+      for (int e = 1; e < EG; ++e) v = fmaxf(v, y[k * EG + e]);
+      if constexpr (G == 32) v = halves<true>(v);
+      mx[k] = lane_reduce<G, true>(v);
     }
 #pragma unroll
     for (int k = 0; k < NR; ++k) {
       float v = 0.f;
       if (mx[k] != -INFINITY) {
 #pragma unroll
-        for (int e = 0; e < EG; ++e) v += exp2f((x[k * EG + e] - mx[k]) * kLog2e);
+        for (int e = 0; e < EG; ++e) v += exp2f(y[k * EG + e] - mx[k]);
       }
-      if constexpr (G >= 8) v = shfl_add(v, 32);
-#pragma unroll
-      for (int o = 1; o < G; o <<= 1) v = shfl_add(v, o);
-      sm[k] = v;
+      if constexpr (G == 32) v = halves<false>(v);
+      sm[k] = lane_reduce<G, false>(v);
     }
   }
-  // first row (within the 32 x 32 product) of the lane's k-th row group
-  __device__ __forceinline__ static int row_of(int k, int hi) {
-    const int e = k * EG;
-    return 8 * (e >> 2) + (G >= 8 ? 0 : 4 * hi) + (e & 3);
-  }
 };
+
+// LDS chunk swizzles of staged rows (4 chunks of 16 bytes per 64-byte row):
+// eight lanes reading one logical chunk of rows {0..3, 16..19} + 4 j (Q',
+// permuted) or of rows 0..7 + 8 j (K') hit eight different bank groups.
+__device__ __forceinline__ int swz_a(int row) { return ((row >> 1) & 1) | ((row >> 3) & 2); }
+__device__ __forceinline__ int swz_b(int row) { return (row >> 1) & 3; }
 
 // Group size of the epilogue, and whether a group is a whole block pair
 // (blocks of at most 32 groups) or a 32 x 32 part of one.
@@ -185,8 +209,8 @@ __global__ __launch_bounds__(256, 2) void antidiag_kernel(AdArgs a) {
 
   // ---- DMA roles: DMA k of a stage moves 16 staged rows (1 KiB); lane L
   // lands at row 16 k + L / 4, LDS chunk L % 4, which holds the row's logical
-  // chunk (L % 4) ^ ((row >> 1) & 3): the operand reads below are free of
-  // bank conflicts
+  // chunk (L % 4) ^ swizzle(row) (swz_a for Q' rows, swz_b for K' rows): the
+  // operand reads below are free of bank conflicts
   const int64_t qrow = int64_t(a.Hq) * D * 2, krow = int64_t(a.Hkv) * D * 2;
   const int drow = lane >> 2;
   const char *qtile = a.q + (int64_t(t0) + int64_t(r0) * S) * qrow + int64_t(h) * D * 2;
@@ -199,14 +223,14 @@ __global__ __launch_bounds__(256, 2) void antidiag_kernel(AdArgs a) {
 #pragma unroll
     for (int x = 0; x < kDmaA; ++x) {
       const int row = 16 * (w + 4 * x) + drow;
-      const int chunk = (lane & 3) ^ ((row >> 1) & 3);
+      const int chunk = (lane & 3) ^ swz_a(row);
       const int tok = min(row * S + S - 1 - u, qlim);
       dma16(qtile + qt * 64, uint32_t(tok) * uint32_t(qrow) + chunk * 16, sb + (w + 4 * x) * 1024);
     }
 #pragma unroll
     for (int x = 0; x < kDmaB; ++x) {
       const int row = 16 * (w + 4 * x) + drow;
-      const int chunk = (lane & 3) ^ ((row >> 1) & 3);
+      const int chunk = (lane & 3) ^ swz_b(row);
       const int tok = min(row * S + u, klim);
       dma16(ktile + qt * 64, uint32_t(tok) * uint32_t(krow) + chunk * 16,
             sb + kAB + (w + 4 * x) * 1024);
@@ -228,18 +252,23 @@ __global__ __launch_bounds__(256, 2) void antidiag_kernel(AdArgs a) {
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
   // rows wholly above the causal boundary or past the sequence: no products
   const bool idle = r0 + 64 * w + 63 < c0 || r0 + 64 * w >= ng;
+  // Q' operand rows are read permuted: the product's row 8 a + 4 h + c
+  // (a = 0..3, h, c = 0..3) takes Q' row 16 h + 4 a + c of its 32, so that
+  // lane (n, hi) ends up holding rows 16 hi + e of column n
+  const int prow = 16 * ((n32 >> 2) & 1) + 4 * (n32 >> 3) + (n32 & 3);
   auto compute = [&](int buf) {
     const char *A = lds + buf * kStage, *Bm = A + kAB;
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
-      const int chunk = ((2 * kk + hi) ^ ((n32 >> 1) & 3)) << 4;
+      const int ca = ((2 * kk + hi) ^ swz_a(prow)) << 4;
+      const int cb = ((2 * kk + hi) ^ swz_b(n32)) << 4;
       bf16x8 af[2], bfr[4];
 #pragma unroll
       for (int m = 0; m < 2; ++m)
-        af[m] = *reinterpret_cast<const bf16x8 *>(A + (64 * w + 32 * m + n32) * kSRow + chunk);
+        af[m] = *reinterpret_cast<const bf16x8 *>(A + (64 * w + 32 * m + prow) * kSRow + ca);
 #pragma unroll
       for (int n = 0; n < 4; ++n)
-        bfr[n] = *reinterpret_cast<const bf16x8 *>(Bm + (32 * n + n32) * kSRow + chunk);
+        bfr[n] = *reinterpret_cast<const bf16x8 *>(Bm + (32 * n + n32) * kSRow + cb);
 #pragma unroll
       for (int m = 0; m < 2; ++m)
 #pragma unroll
@@ -249,12 +278,11 @@ __global__ __launch_bounds__(256, 2) void antidiag_kernel(AdArgs a) {
   };
 
   // diagonal entries (r == c): product (m, ndg + m) of this wavefront, lane
-  // (n32, hi) holding the one at element e_diag if any
+  // (n32, hi) holding the one at element e_diag = n32 - 16 hi if any
   const int ndg = 2 * w - 4 * (ct - 2 * rt);
   const bool diag_wave = ndg > -2 && ndg < 4;
-  const int xd = n32 - 4 * hi;
-  const bool has_diag = xd >= 0 && (xd & 4) == 0;
-  const int e_diag = ((xd >> 3) << 2) | (xd & 3);
+  const int e_diag = n32 - 16 * hi;
+  const bool has_diag = e_diag >= 0 && e_diag < 16;
   const int st_freeze = ((S + 1) >> 1) * QTR - 1;
   float frozen[2] = {0.f, 0.f};
 
@@ -307,7 +335,8 @@ __global__ __launch_bounds__(256, 2) void antidiag_kernel(AdArgs a) {
   // every sample of the tile exists and counts S pairs: all key groups before
   // all query groups, all query groups full
   const bool interior = c0 + kTN <= r0 && (r0 + kTM) * S <= len;
-  const float fscale = a.scale / float(S);
+  const float lscale = a.scale * kLog2e;   // samples kept in log2 units
+  const float fscale = lscale / float(S);
 
   auto finish = [&](auto grp) __attribute__((always_inline)) {
     using Gr = decltype(grp);
@@ -328,7 +357,8 @@ __global__ __launch_bounds__(256, 2) void antidiag_kernel(AdArgs a) {
         STEM_AD_TAKE(4) STEM_AD_TAKE(5) STEM_AD_TAKE(6) STEM_AD_TAKE(7)
 #undef STEM_AD_TAKE
       }
-      const int rb = r0 + 64 * w + 32 * m, cb = c0 + 32 * n;
+      const int rb = r0 + 64 * w + 32 * m + 16 * hi, cb = c0 + 32 * n;
+      // samples in log2 units: y = acc * scale * log2(e) / pairs
       if (idle) {
 #pragma unroll
         for (int e = 0; e < 16; ++e) x[e] = -INFINITY;
@@ -338,24 +368,24 @@ __global__ __launch_bounds__(256, 2) void antidiag_kernel(AdArgs a) {
       } else {
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-          const int r = rb + 8 * (e >> 2) + 4 * hi + (e & 3), c = cb + n32;
+          const int r = rb + e, c = cb + n32;
           const int cnt = (r < ng && c <= r) ? pair_count(r, c, S, len) : 0;
-          x[e] = cnt > 0 ? x[e] * (a.scale / float(cnt)) : -INFINITY;
+          x[e] = cnt > 0 ? x[e] * (lscale / float(cnt)) : -INFINITY;
         }
       }
       float mx[R::NR], sm[R::NR];
       R::reduce(x, mx, sm);
       if constexpr (G < 32 || Gr::kWhole) {
         // whole block pairs: lanes at the first column of a group write
-        if (n32 % G == 0 && (G < 8 || hi == 0)) {
+        if (n32 % G == 0 && (G < 32 || hi == 0)) {
 #pragma unroll
           for (int k = 0; k < R::NR; ++k) {
-            const int i = (rb + R::row_of(k, hi)) / G, j = (cb + n32) / G;
+            const int i = (rb + k * R::EG) / G, j = (cb + n32) / G;
             if (i < nb && j <= i) {
               float tv = -INFINITY;
               if (mx[k] != -INFINITY) {
                 const int ns = interior ? G * G : pair_samples(i, j, G, ng, S, len);
-                tv = mx[k] + __logf(sm[k] / float(ns));
+                tv = (mx[k] + __log2f(sm[k] / float(ns))) * kLn2;
               }
               orow[int64_t(i) * (i + 1) / 2 + j] = tv;
             }
@@ -400,9 +430,9 @@ __global__ __launch_bounds__(256, 2) void antidiag_kernel(AdArgs a) {
         for (int x = 0; x < per; ++x)
           for (int y = 0; y < per; ++y) {
             const f32x2 pv = part[(ib * per + x) * 4 + jb * per + y];
-            if (pv[0] != -INFINITY) sum += pv[1] * exp2f((pv[0] - mx) * kLog2e);
+            if (pv[0] != -INFINITY) sum += pv[1] * exp2f(pv[0] - mx);
           }
-        t = mx + __logf(sum / float(pair_samples(i, j, gpb, ng, S, len)));
+        t = (mx + __log2f(sum / float(pair_samples(i, j, gpb, ng, S, len)))) * kLn2;
       }
       orow[int64_t(i) * (i + 1) / 2 + j] = t;
     }
@@ -431,7 +461,6 @@ __global__ __launch_bounds__(256) void antidiag_metric_kernel(MetricArgs a) {
   float *x = a.scores + int64_t(h) * a.per_head + a.pd.tri[s] + int64_t(i) * (i + 1) / 2;
   const float *wv = a.vnorm + int64_t(hk) * a.nbT + b0;
   const int n = i + 1;
-  constexpr float kLog2e = 1.4426950408889634f;
   if (a.mode == STEM_METRIC_ADDITIVE) {
     for (int j = lane; j < n; j += 64) {
       const float wj = wv[j];
