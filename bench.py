@@ -58,12 +58,13 @@ def attn_flops(plan, diag_half: bool) -> float:
     return full - 0.5 * per_tile * i.total_blocks * i.num_q_heads
 
 
-def traffic_record(workload: str):
-    """HBM bytes per attention launch measured by rocprofv3 (FETCH_SIZE and
-    WRITE_SIZE, copy-calibrated) and recorded under profiles/; returned only
-    if the attention kernel source is unchanged since that measurement."""
-    path = os.path.join(ROOT, "profiles", f"attn_{workload}.md")
-    src = os.path.join(ROOT, "block_sparse_causal_amd", "csrc", "attn.hip")
+def traffic_record(workload: str, profile: str = None, source: str = "attn.hip"):
+    """HBM bytes per launch of a kernel measured by rocprofv3 (FETCH_SIZE and
+    WRITE_SIZE, copy-calibrated) and recorded under profiles/ (by default the
+    attention kernel's); returned only if the kernel's source is unchanged
+    since that measurement."""
+    path = os.path.join(ROOT, "profiles", profile or f"attn_{workload}.md")
+    src = os.path.join(ROOT, "block_sparse_causal_amd", "csrc", source)
     try:
         rec = None
         for line in open(path):
@@ -385,8 +386,11 @@ def main():
         result["config"]["score"] = f"antidiag stride {args.score_stride}"
         # the score stage is stem_score_antidiag: the sample products plus
         # the row-softmax kernel
+        arec = traffic_record(name, f"antidiag_{name}_stride{args.score_stride}.md", "antidiag.hip")
         result["antidiag"] = {"bound": "mfma", "achieved": round(ach, 2), "peak": peak,
                               "unit": "TFLOP/s", "frac": round(ach / peak, 4),
+                              "traffic": (None if arec is None
+                                          else arec["fetch_bytes"] + arec["write_bytes"]),
                               "flop_per_launch": af, "avg_launch_ms": round(stage_ms["score"], 4)}
         log(f"antidiag stride {args.score_stride}: {stage_ms['score']:.3f} ms, {ach:.1f} TFLOP/s")
     del bufs
