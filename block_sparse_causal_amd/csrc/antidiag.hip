@@ -439,6 +439,71 @@ __global__ __launch_bounds__(256, 2) void antidiag_kernel(AdArgs a) {
   }
 }
 
+// ---- f32 inputs: one workgroup per (query head, query block) row, each
+// thread forming whole samples from f32 dot products (the f32 workloads are
+// small; no matrix cores), block pairs reduced with an online max / sum
+// merged across the workgroup.
+__device__ __forceinline__ void lse_merge(float &m, float &s, float m2, float s2) {
+  const float mn = fmaxf(m, m2);
+  if (mn == -INFINITY) return;
+  s = (m == -INFINITY ? 0.f : s * __expf(m - mn)) + (m2 == -INFINITY ? 0.f : s2 * __expf(m2 - mn));
+  m = mn;
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void antidiag_f32_kernel(AdArgs a) {
+  __shared__ float red_m[4], red_s[4];
+  __shared__ int red_n[4];
+  const int h = blockIdx.y, b = blockIdx.x;
+  const int s = a.pd.blk_seq[b];
+  const int i = b - a.pd.cu_blocks[s];
+  const int S = a.stride, gpb = a.block / S;
+  const int t0 = a.pd.cu_seqlens[s];
+  const int len = a.pd.cu_seqlens[s + 1] - t0;
+  const int ng = (len + S - 1) / S;
+  const int hk = h / a.G;
+  const float *q = reinterpret_cast<const float *>(a.q) + (int64_t(t0) * a.Hq + h) * D;
+  const float *k = reinterpret_cast<const float *>(a.k) + (int64_t(t0) * a.Hkv + hk) * D;
+  const int64_t qs = int64_t(a.Hq) * D, ks = int64_t(a.Hkv) * D;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  float *orow = a.out + int64_t(h) * a.per_head + a.pd.tri[s] + int64_t(i) * (i + 1) / 2;
+  for (int j = 0; j <= i; ++j) {
+    float m = -INFINITY, sm = 0.f;
+    int ns = 0;
+    for (int x = tid; x < gpb * gpb; x += 256) {
+      const int r = i * gpb + x / gpb, c = j * gpb + x % gpb;
+      if (r >= ng || c > r) continue;
+      float acc = 0.f;
+      int cnt = 0;
+      for (int u = 0; u < S; ++u) {
+        const int qp = r * S + S - 1 - u, kp = c * S + u;
+        if (qp >= len || kp >= len || kp > qp) continue;
+        const float *qv = q + qp * qs, *kv = k + kp * ks;
+        for (int e = 0; e < D; ++e) acc = fmaf(qv[e], kv[e], acc);
+        ++cnt;
+      }
+      if (cnt == 0) continue;
+      lse_merge(m, sm, acc * (a.scale / float(cnt)), 1.f);
+      ++ns;
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      const float m2 = __shfl_xor(m, o), s2 = __shfl_xor(sm, o);
+      ns += __shfl_xor(ns, o);
+      lse_merge(m, sm, m2, s2);
+    }
+    if (lane == 0) { red_m[w] = m; red_s[w] = sm; red_n[w] = ns; }
+    __syncthreads();
+    if (tid == 0) {
+      float mt = red_m[0], st = red_s[0];
+      int nt = red_n[0];
+      for (int x = 1; x < 4; ++x) { lse_merge(mt, st, red_m[x], red_s[x]); nt += red_n[x]; }
+      orow[j] = nt > 0 ? mt + __logf(st / float(nt)) : -INFINITY;
+    }
+    __syncthreads();
+  }
+}
+
 // ---- metric rows from block logits, in place
 struct MetricArgs {
   float *scores;
@@ -522,12 +587,20 @@ hipError_t launch_score_antidiag(const stem_plan_info &in, PlanDev pd, const voi
   a.units_per_head = static_cast<int32_t>(antidiag_units_per_head(in, stride));
   a.per_head = in.score_elems_per_head;
   a.scale = 1.0f / sqrtf(float(in.head_dim));
-  const int64_t units = int64_t(in.num_q_heads) * a.units_per_head;
-  const unsigned grid = static_cast<unsigned>((units + 7) / 8 * 8);
-  if (in.head_dim == 128)
-    hipLaunchKernelGGL(antidiag_kernel<128>, dim3(grid), dim3(256), 0, st, a);
-  else
-    hipLaunchKernelGGL(antidiag_kernel<64>, dim3(grid), dim3(256), 0, st, a);
+  if (in.dtype == STEM_F32) {
+    const dim3 grid(static_cast<unsigned>(in.total_blocks), static_cast<unsigned>(in.num_q_heads));
+    if (in.head_dim == 128)
+      hipLaunchKernelGGL(antidiag_f32_kernel<128>, grid, dim3(256), 0, st, a);
+    else
+      hipLaunchKernelGGL(antidiag_f32_kernel<64>, grid, dim3(256), 0, st, a);
+  } else {
+    const int64_t units = int64_t(in.num_q_heads) * a.units_per_head;
+    const unsigned grid = static_cast<unsigned>((units + 7) / 8 * 8);
+    if (in.head_dim == 128)
+      hipLaunchKernelGGL(antidiag_kernel<128>, dim3(grid), dim3(256), 0, st, a);
+    else
+      hipLaunchKernelGGL(antidiag_kernel<64>, dim3(grid), dim3(256), 0, st, a);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
 

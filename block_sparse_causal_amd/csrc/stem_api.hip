@@ -66,17 +66,18 @@ extern "C" int stem_score_antidiag(const stem_plan_info *in, const void *plan_de
                                    float *scores, void *stream) {
   int rc = check_info(in, plan_dev);
   if (rc) return rc;
-  if (in->dtype != STEM_BF16) return STEM_EUNSUPPORTED;
   if (stride < 1 || stride > in->block || (stride & (stride - 1))) return STEM_EINVAL;
   if (in->total_blocks == 0) return STEM_OK;
   if (!q || !k || !vnorm || !scores) return STEM_EINVAL;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(vnorm, 4) || !aligned(scores, 4))
     return STEM_EINVAL;
-  if (int64_t(in->num_q_heads) * antidiag_units_per_head(*in, stride) > INT32_MAX / 2)
-    return STEM_EUNSUPPORTED;
-  // token rows of one tile must be addressable with 32-bit offsets
-  if (int64_t(256) * stride * in->num_q_heads * in->head_dim * 2 + 64 > (int64_t(1) << 32))
-    return STEM_EUNSUPPORTED;
+  if (in->dtype == STEM_BF16) {
+    if (int64_t(in->num_q_heads) * antidiag_units_per_head(*in, stride) > INT32_MAX / 2)
+      return STEM_EUNSUPPORTED;
+    // token rows of one tile must be addressable with 32-bit offsets
+    if (int64_t(256) * stride * in->num_q_heads * in->head_dim * 2 + 64 > (int64_t(1) << 32))
+      return STEM_EUNSUPPORTED;
+  }
   return hip_status(launch_score_antidiag(*in, make_plan_dev(*in, plan_dev), q, k, vnorm, stride,
                                           scores, static_cast<hipStream_t>(stream)));
 }

@@ -267,8 +267,9 @@ def stem_score(plan: Plan, qbar, kbar, vnorm, scores, stream=None) -> None:
 def stem_score_antidiag(plan: Plan, q, k, vnorm, stride: int, scores, stream=None) -> None:
     import torch
     i = plan.info
-    _need(q, "q", torch.bfloat16, (i.total_tokens, i.num_q_heads, i.head_dim))
-    _need(k, "k", torch.bfloat16, (i.total_tokens, i.num_kv_heads, i.head_dim))
+    dt = _io_dtype(plan)
+    _need(q, "q", dt, (i.total_tokens, i.num_q_heads, i.head_dim))
+    _need(k, "k", dt, (i.total_tokens, i.num_kv_heads, i.head_dim))
     _need(vnorm, "vnorm", torch.float32, (i.num_kv_heads, i.total_blocks))
     _need(scores, "scores", torch.float32, (i.num_q_heads, i.score_elems_per_head))
     _check("stem_score_antidiag",

@@ -185,11 +185,12 @@ int stem_score(const stem_plan_info *info, const void *plan_dev,
  * there are none) and takes the place of s_ij in the metric mode of the plan.
  * A row whose logits are all -inf gets 0 in the softmax forms.  S = 1 gives
  * the exact log-mean-exp of each block pair's causal token logits.
- *   q [T, Hq, d], k [T, Hkv, d]: bf16 only (STEM_EUNSUPPORTED for f32 plans),
- *   16-byte aligned; vnorm [Hkv, nbT] f32 from stem_pool; scores as for
- *   stem_score (fully overwritten).  STEM_EINVAL for a bad stride;
+ *   q [T, Hq, d], k [T, Hkv, d]: the plan's dtype, 16-byte aligned; vnorm
+ *   [Hkv, nbT] f32 from stem_pool; scores as for stem_score (fully
+ *   overwritten).  STEM_EINVAL for a bad stride; for bf16 plans
  *   STEM_EUNSUPPORTED when the work bound Hq * tile pairs reaches 2^30 or
- *   256 * stride token rows of Q span 4 GiB. */
+ *   256 * stride token rows of Q span 4 GiB.  bf16 runs on the matrix
+ *   cores; f32 (small problems) forms each sample with f32 dot products. */
 int stem_score_antidiag(const stem_plan_info *info, const void *plan_dev,
                         const void *q, const void *k, const float *vnorm, int32_t stride,
                         float *scores, void *stream);

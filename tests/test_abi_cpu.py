@@ -206,7 +206,7 @@ def test_antidiag_score_rejects_bad_arguments_before_any_launch():
     assert A(ctypes.byref(info), P, P + 8, P, P, 4, P, None) == stem.STEM_EINVAL
     assert A(ctypes.byref(info), P, P, P, P + 2, 4, P, None) == stem.STEM_EINVAL
     f32 = stem.plan_for(syn.custom([256], 4, 2, 64, "f32", 64)).info
-    assert A(ctypes.byref(f32), P, P, P, P, 4, P, None) == stem.STEM_EUNSUPPORTED
+    assert A(ctypes.byref(f32), P, P, P, P, 3, P, None) == stem.STEM_EINVAL
     # stride 1 on the longest sequence with many heads exceeds the work bound
     big = stem.plan_for(syn.custom([64 * 4096], 1024, 1, 64, "bf16", 64)).info
     assert A(ctypes.byref(big), P, P, P, P, 1, P, None) == stem.STEM_EUNSUPPORTED

@@ -5,7 +5,8 @@ attends with it.
 Small workloads are checked on every metric row and every selection row,
 over strides from 1 (every causal token pair) to the block size (one group
 per block), ragged and empty sequences, sequences too short to hold a
-sample, B = 64 / 128, d = 64 / 128 and the three metric forms.  The 128K
+sample, B = 64 / 128, d = 64 / 128, bf16 and f32 inputs and the three metric
+forms.  The 128K
 layer runs in the benchmark's configuration (stride 16) and is checked on
 sampled metric rows, every selection row and sampled attention rows.
 """
@@ -37,13 +38,20 @@ W = {
                                  sink_blocks=0, k_min=1, rho0=0.2, tau=3.0, seed=34),
     "b64-d128-tiny": syn.custom([1, 3, 5, 9, 67, 0, 130], 2, 1, 128, "bf16", 64,
                                 sink_blocks=1, k_min=2, rho0=0.5, tau=2.0, seed=35),
+    "f32-b64-d64": syn.custom([1024, 100], 2, 1, 64, "f32", 64, rope_theta=None,
+                              sink_blocks=1, k_min=2, rho0=1.0, tau=4.0, seed=37),
+    "f32-b128-d128": syn.custom([700, 129, 3], 2, 2, 128, "f32", 128,
+                                sink_blocks=2, k_min=1, rho0=0.0, tau=1.0, seed=38),
+    "single-head-1k-fp32": syn.WORKLOADS["single-head-1k-fp32"],
 }
 
 CASES = [("b64-d128-varlen", 1), ("b64-d128-varlen", 4), ("b64-d128-varlen", 64),
          ("b128-d128-gqa4", 2), ("b128-d128-gqa4", 16), ("b128-d128-gqa4", 128),
          ("b64-d64-gqa7", 8), ("b64-d64-gqa7", 32),
          ("b128-d64-short", 4), ("b128-d64-short", 64),
-         ("b64-d128-tiny", 8), ("b64-d128-tiny", 16)]
+         ("b64-d128-tiny", 8), ("b64-d128-tiny", 16),
+         ("f32-b64-d64", 4), ("f32-b64-d64", 16), ("f32-b128-d128", 1), ("f32-b128-d128", 32),
+         ("single-head-1k-fp32", 16)]
 
 
 def _check(w, stride, n_attn_rows=24):
@@ -100,10 +108,6 @@ def test_antidiag_rejects_bad_arguments():
         with pytest.raises(stem.StemError) as e:
             stem.stem_score_antidiag(plan, q, k, vn, bad, sc)
         assert e.value.status == stem.STEM_EINVAL
-    f32 = stem.plan_for(syn.custom([100], 2, 1, 64, "f32", 64)).to("cuda")
-    rc = stem.lib().stem_score_antidiag(stem.ctypes.byref(f32.info), f32.dev_ptr, q.data_ptr(),
-                                        k.data_ptr(), vn.data_ptr(), 4, sc.data_ptr(), None)
-    assert rc == stem.STEM_EUNSUPPORTED
 
 
 @pytest.mark.timeout(900)
