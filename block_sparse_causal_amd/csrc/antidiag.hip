@@ -454,7 +454,8 @@ template <int D>
 __global__ __launch_bounds__(256) void antidiag_f32_kernel(AdArgs a) {
   __shared__ float red_m[4], red_s[4];
   __shared__ int red_n[4];
-  const int h = blockIdx.y, b = blockIdx.x;
+  const int nbT = a.pd.cu_blocks[a.num_seqs];
+  const int h = int(blockIdx.x / unsigned(nbT)), b = int(blockIdx.x - unsigned(h) * unsigned(nbT));
   const int s = a.pd.blk_seq[b];
   const int i = b - a.pd.cu_blocks[s];
   const int S = a.stride, gpb = a.block / S;
@@ -584,11 +585,12 @@ hipError_t launch_score_antidiag(const stem_plan_info &in, PlanDev pd, const voi
   a.block = in.block;
   a.stride = stride;
   a.num_seqs = in.num_seqs;
-  a.units_per_head = static_cast<int32_t>(antidiag_units_per_head(in, stride));
+  a.units_per_head = in.dtype == STEM_BF16 ? static_cast<int32_t>(antidiag_units_per_head(in, stride)) : 0;
   a.per_head = in.score_elems_per_head;
   a.scale = 1.0f / sqrtf(float(in.head_dim));
   if (in.dtype == STEM_F32) {
-    const dim3 grid(static_cast<unsigned>(in.total_blocks), static_cast<unsigned>(in.num_q_heads));
+    // one workgroup per (head, block) row; Hq * nbT < 2^31 (plan limit)
+    const dim3 grid(static_cast<unsigned>(in.total_blocks * in.num_q_heads));
     if (in.head_dim == 128)
       hipLaunchKernelGGL(antidiag_f32_kernel<128>, grid, dim3(256), 0, st, a);
     else
