@@ -110,6 +110,36 @@ def test_antidiag_rejects_bad_arguments():
         assert e.value.status == stem.STEM_EINVAL
 
 
+def _full_size_rows(w, stride, n_rows, seed):
+    H.log(f"case antidiag full-size {w.name} stride {stride}: generating inputs")
+    r = H.GpuRun(w, out_dtype="bf16", score_stride=stride)
+    H.log("  GPU done; metric rows (sampled)")
+    wv = O.pool_vnorm(r.x.v, w.cu_seqlens, w.block)
+    offs, _ = O.score_offsets(r.cu_blocks)
+    seq_of = np.repeat(np.arange(len(r.cu_blocks) - 1), np.diff(r.cu_blocks))
+    G = w.num_q_heads // w.num_kv_heads
+    for (h, b) in H.sample_rows(r, n_rows, seed=seed):
+        s = int(seq_of[b]); i = b - int(r.cu_blocks[s])
+        b0 = int(r.cu_blocks[s])
+        t = O.antidiag_row_logits(r.x.q, r.x.k, w.cu_seqlens, w.block, stride, h, s, i)
+        ref = O.metric_from_logits(t, wv[h // G, b0:b0 + i + 1], w.metric, w.beta)
+        got = r.scores[h, int(offs[s]) + O.tri(i):][:i + 1]
+        H.check_scores(got, ref, w.dtype, f"antidiag scores {(h, b)}", w.metric)
+    H.log("  selection rows (all)")
+    H.select_rows_crossfed(r, H.all_rows(r))
+    H.log("  attention rows (sampled)")
+    worst, lw = H.attn_rows_crossfed(r, H.sample_rows(r, 32, seed=seed + 1))
+    H.log(f"  attention max err {worst:.3g}, lse {lw:.3g}")
+
+
+@pytest.mark.timeout(900)
+def test_antidiag_full_size_varlen():
+    """The packed batch of four sequences (8K, 16K, 32K, 64K tokens, B = 64) at
+    stride 8: many sequences in one launch, each with its own tiles."""
+    _cuda()
+    _full_size_rows(syn.WORKLOADS["llama3-8b-varlen-120k-b64"], 8, 24, seed=7)
+
+
 @pytest.mark.timeout(900)
 def test_antidiag_full_size_128k():
     """The 128K Llama-3-8B-shaped layer (32/8 heads, d = 128, B = 128) at
