@@ -17,6 +17,7 @@ from block_sparse_causal_amd import stem
 from block_sparse_causal_amd import synthetic as syn
 from oracle import stem_oracle as O
 from tests import _harness as H
+from tests._golden import pages_parameters
 
 pytestmark = pytest.mark.gpu
 
@@ -80,7 +81,7 @@ def test_antidiag_every_row(name, stride):
 @pytest.mark.parametrize("metric", ["additive", "routing"])
 def test_antidiag_metric_forms(metric):
     _cuda()
-    _check(W["b64-d128-varlen"].replace(metric=metric, beta=0.2), 8)
+    _check(W["b64-d128-varlen"].replace(metric=metric, beta=pages_parameters()["beta"]), 8)
 
 
 def test_antidiag_rows_without_samples():

@@ -14,6 +14,7 @@ from block_sparse_causal_amd import stem
 from block_sparse_causal_amd import synthetic as syn
 from oracle import stem_oracle as O
 from tests import _harness as H
+from tests._golden import pages_parameters
 
 pytestmark = pytest.mark.gpu
 
@@ -256,8 +257,9 @@ def test_full_size_additive_metric_linear_budget():
     """The 32K layer with the pages' additive metric and linear budget, at the
     ablation's best values beta = 0.2 and mu = 0.7."""
     _cuda()
-    _full_size("llama3-8b-32k-b64", 64, metric="additive", beta=0.2, budget_mode="linear",
-               k_start=24.0, mu=0.7)
+    pp = pages_parameters()
+    _full_size("llama3-8b-32k-b64", 64, metric="additive", beta=pp["beta"], budget_mode="linear",
+               k_start=24.0, mu=pp["mu"])
 
 
 @pytest.mark.timeout(900)

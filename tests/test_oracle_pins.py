@@ -10,6 +10,7 @@ import scipy.special
 import torch
 
 from oracle import stem_oracle as O
+from tests._golden import pages_parameters
 from block_sparse_causal_amd import synthetic as syn
 
 
@@ -263,7 +264,10 @@ def test_budget_closed_forms():
 
 
 def test_budget_linear_endpoints():
-    b = O.budget_linear(101, 2, 0, 20, 0.7)
+    # mu of the pages' ablation (tests/golden/pages_parameters.txt): 0.7
+    mu = pages_parameters()["mu"]
+    assert mu == 0.7
+    b = O.budget_linear(101, 2, 0, 20, mu)
     assert b[2] == 3                               # row 2 has only 3 causal blocks
     assert b[50] == 2 + 1 + math.ceil(20 * 0.5 + 14 * 0.5)
     assert b[100] == 2 + 1 + 14                    # k_end = mu * k_start
