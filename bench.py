@@ -232,11 +232,12 @@ def copy_calibration(nbytes: int = 1 << 30):
 SWEEP_TOKENS = (8192, 16384, 32768, 65536, 131072)
 
 
-def sweep(base_name: str, steps: int, warmup: int, dense_reps: int):
+def sweep(base_name: str, steps: int, warmup: int, dense_reps: int, score_stride=None):
     """Latency of the whole path and of the dense comparator (the same
     attention kernel with every causal block kept) at growing context length,
-    with the head shape and Stem parameters of ``base_name``.  One JSON line
-    per length, then a summary line."""
+    with the head shape and Stem parameters of ``base_name`` (and the sampled
+    metric at ``score_stride`` if given).  One JSON line per length, then a
+    summary line."""
     import torch
     from block_sparse_causal_amd import stem
     from block_sparse_causal_amd import synthetic as syn
@@ -251,7 +252,7 @@ def sweep(base_name: str, steps: int, warmup: int, dense_reps: int):
         del x
         plan = stem.plan_for(w).to("cuda")
         bufs = stem.Buffers(plan, "cuda", out_dtype=torch.bfloat16)
-        _, stage, total = time_path(plan, q, k, v, bufs, steps, warmup)
+        _, stage, total = time_path(plan, q, k, v, bufs, steps, warmup, score_stride=score_stride)
         del bufs
         step_ms = float(np.mean(total))
         attn_ms = float(np.mean(stage[3]))
@@ -266,6 +267,10 @@ def sweep(base_name: str, steps: int, warmup: int, dense_reps: int):
                "dense_attn_ms": round(dms, 3),
                "dense_attn_tflops": round(dflops / (dms * 1e-3) / 1e12, 1),
                "speedup": round(dms / step_ms, 2)}
+        if score_stride is not None:
+            af = antidiag_flops(w, score_stride)
+            row["score_stride"] = score_stride
+            row["antidiag_tflops"] = round(af / (float(np.mean(stage[1])) * 1e-3) / 1e12, 1)
         log(f"sweep {tokens:>6} tokens: stem {step_ms:.3f} ms, dense {dms:.3f} ms, "
             f"speed-up {dms / step_ms:.2f}x")
         print(json.dumps({"sweep": base_name, **row}), flush=True)
@@ -307,7 +312,7 @@ def main():
 
     name = args.workload or syn.HEADLINE
     if args.sweep:
-        sweep(name, args.steps, args.warmup, args.dense_reps)
+        sweep(name, args.steps, args.warmup, args.dense_reps, args.score_stride)
         return
     w = syn.WORKLOADS[name]
     log(f"workload {name}: generating seeded inputs")
