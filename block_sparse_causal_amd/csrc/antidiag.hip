@@ -18,13 +18,15 @@
 // cores (v_mfma_f32_32x32x16_bf16, f32 accumulation), each wavefront 64 rows
 // x 128 columns (eight 32 x 32 products: 6 KiB of LDS operand reads per 8
 // products).  Operands arrive by global->LDS DMA, 32 dimensions of one token
-// position u per stage (24 KiB), three stages in flight; two workgroups share
-// a CU, so one's epilogue overlaps the other's products.  Block pairs never
-// straddle a tile (its sides are whole numbers of blocks), so the tile
-// finishes its block logits itself, in registers: within each 32 x 32
-// product the samples of a block pair (or of its 32 x 32 part, combined
-// through LDS when blocks hold more than 32 groups) are reduced to a max and
-// a sum of exponentials by in-lane steps and cross-lane shuffles.
+// position u per stage (24 KiB), three stage buffers with the loads two
+// stages ahead; two workgroups share a CU, so one's epilogue overlaps the
+// other's products.  Block pairs never straddle a tile (its sides are whole
+// numbers of blocks), so the tile finishes its block logits itself, in
+// registers: the Q' operand rows are read in a permuted order that leaves
+// each lane holding 16 consecutive group rows of one column, so within each
+// 32 x 32 product the samples of a block pair (or of its 32 x 32 part,
+// combined through LDS when blocks hold more than 32 groups) reduce to a max
+// and a sum of exponentials in the lane and across lanes by DPP.
 //
 // Only the tiles on the diagonal hold samples whose anti-diagonal crosses the
 // causal boundary (r = c): there the pairs with u >= ceil(S/2) have the key
@@ -33,6 +35,9 @@
 // clamped to its last token and their samples masked; in the tiles holding a
 // short last group, the staged rows of its missing tokens are zeroed, so each
 // sample sums exactly its own pairs and is divided by its own pair count.
+//
+// f32 inputs take antidiag_f32_kernel instead: one workgroup per metric row,
+// each thread forming whole samples from f32 dot products.
 //
 // Kernel 2 (antidiag_metric_kernel): one wavefront per metric row turns the
 // row's block logits into the metric in place (row softmax times V magnitude,
