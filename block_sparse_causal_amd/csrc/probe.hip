@@ -1,4 +1,4 @@
-// Measurement probes: the ceilings the path's kernels are judged against,
+// Measurement probes: the ceilings the path's kernels are compared with,
 // re-measured on the device at hand (not part of the prefill path).
 //
 //   stem_probe_mfma      back-to-back v_mfma_f32_32x32x16_bf16 on every SIMD
