@@ -95,6 +95,19 @@ def test_antidiag_rows_without_samples():
     assert np.all(r.idx[:, 0, 0] == 0) and np.all(r.idx[:, 1, 0] == 0)
 
 
+def test_antidiag_many_sequences():
+    # 150 short sequences of mixed lengths (empty, shorter than a group,
+    # ragged) in one launch: every kernel walks the sequence table
+    _cuda()
+    rng = np.random.default_rng(41)
+    lens = [int(x) for x in rng.integers(0, 300, size=150)]
+    lens[:4] = [0, 1, 7, 64]
+    w = syn.custom(lens, 4, 2, 64, "bf16", 64, sink_blocks=1, k_min=2, rho0=0.5, tau=3.0,
+                   seed=42).replace(name="many-sequences")
+    for stride in (4, 32):
+        _check(w, stride, n_attn_rows=32)
+
+
 def test_antidiag_rejects_bad_arguments():
     import torch
     _cuda()

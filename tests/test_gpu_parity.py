@@ -153,6 +153,19 @@ def test_full_budget_equals_dense_causal(dtype, B, d):
     assert np.abs(r.lse - lse).max() <= H.TOL[dtype]["lse"]
 
 
+def test_many_short_sequences():
+    """150 sequences of 0 to 299 tokens packed in one launch (every stage
+    walks the sequence table), checked on every row."""
+    _cuda()
+    rng = np.random.default_rng(43)
+    lens = [int(x) for x in rng.integers(0, 300, size=150)]
+    lens[:4] = [0, 1, 65, 128]
+    w = syn.custom(lens, 4, 2, 128, "bf16", 64, sink_blocks=2, k_min=1, rho0=0.7, tau=2.0,
+                   seed=44).replace(name="many-sequences")
+    H.log("case many short sequences")
+    _full_check(H.GpuRun(w))
+
+
 def test_edge_shapes():
     """Tiny and degenerate sequences: length 1, shorter than a block, exactly
     one block, empty; no sinks; zero k_min; zero decay."""
