@@ -111,6 +111,12 @@ def lib() -> ctypes.CDLL:
         if not os.path.exists(_LIB_PATH):
             raise RuntimeError(f"{_LIB_PATH} is missing: build it with "
                                "`python -m block_sparse_causal_amd.build`")
+        # torch first: its HIP libraries load their own copy of the HIP runtime
+        # by the unversioned name, which libstem.so's versioned dependency then
+        # resolves to.  Loaded the other way round, the process would hold two
+        # runtimes, and torch's streams and allocations would be foreign to the
+        # one the kernels are launched on.
+        import torch  # noqa: F401
         L = ctypes.CDLL(_LIB_PATH)
         for name, (res, args) in _SIGS.items():
             fn = getattr(L, name)

@@ -29,6 +29,25 @@ def test_library_exports_every_declared_symbol():
         assert hasattr(stem, n), n
 
 
+def test_binding_shares_torchs_hip_runtime():
+    # Loading the library first in a fresh process (no torch imported yet)
+    # must still leave one HIP runtime mapped: the one torch loads.  Two
+    # copies make torch's streams invalid for the library's launches.
+    import subprocess
+    import sys
+    code = ("import re\n"
+            "from block_sparse_causal_amd import stem\n"
+            "stem.lib()\n"
+            "import torch\n"
+            "maps = open('/proc/self/maps').read()\n"
+            "print(sorted(set(re.findall(r'\\S*libamdhip64\\S*', maps))))\n")
+    r = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True,
+                       timeout=300)
+    assert r.returncode == 0, r.stderr[-2000:]
+    paths = eval(r.stdout.strip().splitlines()[-1])
+    assert len(paths) == 1, paths
+
+
 def test_struct_layouts_match_header():
     # offsets follow C layout rules; a mismatch would corrupt every call
     assert ctypes.sizeof(stem.stem_params) == 56
