@@ -359,7 +359,10 @@ void attn_bf16_kernel(AttnArgs a) {
           float bm = -INFINITY;
 #pragma unroll
           for (int q = 0; q < 16; ++q) bm = fmaxf(bm, sacc[u][qt][q]);
-          bm = fmaxf(bm, __shfl_xor(bm, 32));
+          // the lane id comes from inline assembly so that the common path
+          // keeps no copy of it
+          bm = fmaxf(bm, __int_as_float(__builtin_amdgcn_ds_bpermute(
+                             (opaque_lane_id() ^ 32) << 2, __float_as_int(bm))));
           const float mnew = fmaxf(mrun[qt], bm);
           const float alpha =
               mnew == mrun[qt] ? 1.f : __builtin_amdgcn_exp2f((mrun[qt] - mnew) * cl2);
