@@ -218,8 +218,10 @@ void attn_bf16_kernel(AttnArgs a) {
   auto koff_of = [&](int it) {
     return (NCH == 16 && ((it * ROWSTEP) & 8)) ? (koff0 ^ 128u) : koff0;
   };
-  const uint16_t *kbase = static_cast<const uint16_t *>(a.k);
-  const uint16_t *vbase = static_cast<const uint16_t *>(a.v);
+  // K and V rows of this KV head at the sequence's first token
+  const int64_t eseq = (r.seq_start * Hkv + r.g) * int64_t(D);
+  const char *kseq = reinterpret_cast<const char *>(static_cast<const uint16_t *>(a.k) + eseq);
+  const char *vseq = reinterpret_cast<const char *>(static_cast<const uint16_t *>(a.v) + eseq);
   // Stage `part` of block j into buffer `buf`.  Every call issues exactly
   // 2 LOADS DMA instructions (the stage waits count on it): a stage that lies
   // past the end of the sequence (keys all masked, buffer not read) loads
@@ -228,17 +230,31 @@ void attn_bf16_kernel(AttnArgs a) {
     int first = j * B + part * SK;                       // first key (local position)
     int nrows = min(SK, r.seq_len - first);               // may be <= 0 past the end
     if (nrows <= 0) { first = 0; nrows = 1; }
-    const int64_t e0 = ((r.seq_start + first) * Hkv + r.g) * int64_t(D);
-    const uint16_t *kblk = kbase + e0;
-    const uint16_t *vblk = vbase + e0;
+    const size_t off = size_t(static_cast<uint32_t>(first)) * rowbytes;
+    const char *kblk = kseq + off;
+    const char *vblk = vseq + off;
     const uint32_t l0 = lds_base + w * 64 * 16;  // this wavefront's 1 KiB slab
     if (nrows == SK) {
+      if constexpr (LOADS % 2 == 0) {
+        // two load steps (K and V each) per asm block
 #pragma unroll
-      for (int it = 0; it < LOADS; ++it) {
-        const char *kb = reinterpret_cast<const char *>(kblk) + size_t(it) * ROWSTEP * rowbytes;
-        const char *vb = reinterpret_cast<const char *>(vblk) + size_t(it) * ROWSTEP * rowbytes;
-        dma16(kb, koff_of(it), l0 + it * NT * 16 + buf * TILEB);
-        dma16(vb, voff0, l0 + it * NT * 16 + (NBUF + buf) * TILEB);
+        for (int it = 0; it < LOADS; it += 2) {
+          const char *kb = kblk + size_t(it) * ROWSTEP * rowbytes;
+          const char *vb = vblk + size_t(it) * ROWSTEP * rowbytes;
+          const size_t step = size_t(ROWSTEP) * rowbytes;
+          dma16x4(kb, koff_of(it), l0 + it * NT * 16 + buf * TILEB,
+                  vb, voff0, l0 + it * NT * 16 + (NBUF + buf) * TILEB,
+                  kb + step, koff_of(it + 1), l0 + (it + 1) * NT * 16 + buf * TILEB,
+                  vb + step, voff0, l0 + (it + 1) * NT * 16 + (NBUF + buf) * TILEB);
+        }
+      } else {
+#pragma unroll
+        for (int it = 0; it < LOADS; ++it) {
+          const char *kb = kblk + size_t(it) * ROWSTEP * rowbytes;
+          const char *vb = vblk + size_t(it) * ROWSTEP * rowbytes;
+          dma16(kb, koff_of(it), l0 + it * NT * 16 + buf * TILEB);
+          dma16(vb, voff0, l0 + it * NT * 16 + (NBUF + buf) * TILEB);
+        }
       }
     } else if (nrows > 0) {
 #pragma unroll

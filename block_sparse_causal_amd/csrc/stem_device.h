@@ -77,6 +77,35 @@ __device__ __forceinline__ void dma16(const void *gbase, uint32_t voff, uint32_t
       : "memory");
 }
 
+// Four such DMAs in one asm block: M0 is saved and restored once for the
+// four instead of once per instruction (DMA k: base gk, lane offset vk, LDS
+// address lk).
+__device__ __forceinline__ void dma16x4(const void *g0, uint32_t v0, uint32_t l0,
+                                        const void *g1, uint32_t v1, uint32_t l1,
+                                        const void *g2, uint32_t v2, uint32_t l2,
+                                        const void *g3, uint32_t v3, uint32_t l3) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %9\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %5\n\t"
+      "s_mov_b32 m0, %10\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %2, %6\n\t"
+      "s_mov_b32 m0, %11\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %3, %7\n\t"
+      "s_mov_b32 m0, %12\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %4, %8\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(v0), "v"(v1), "v"(v2), "v"(v3), "s"(g0), "s"(g1), "s"(g2), "s"(g3),
+        "s"(l0), "s"(l1), "s"(l2), "s"(l3)
+      : "memory");
+}
+
 // s_waitcnt vmcnt(0) / lgkmcnt(0) alone, as builtins so that the compiler's
 // own wait-count bookkeeping sees them.
 __device__ __forceinline__ void wait_vm() { __builtin_amdgcn_s_waitcnt(0x0F70); }
