@@ -493,8 +493,10 @@ void attn_bf16_kernel(AttnArgs a) {
       const u32x4 v = *reinterpret_cast<const u32x4 *>(ot + row * (D * 2) + ((c ^ (row % NCH)) * 16));
       const int qpos = r.i * B + w * QW + row;
       if (qpos < r.seq_len)
-        *reinterpret_cast<u32x4 *>(static_cast<uint16_t *>(a.out) +
-                                   ((r.seq_start + qpos) * Hq + r.h) * int64_t(D) + c * 8) = v;
+        // non-temporal: O is not read again here, and keeping it out of L2
+        // leaves room for the K/V blocks that neighbouring rows reuse
+        __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(static_cast<uint16_t *>(a.out) +
+                                   ((r.seq_start + qpos) * Hq + r.h) * int64_t(D) + c * 8));
     }
     const int q0 = r.i * B + w * QW + n;
     if (a.lse && hi == 0 && q0 < r.seq_len)
