@@ -88,8 +88,10 @@ __device__ __forceinline__ bool decode_item(const AttnArgs &a, Row &r) {
 // ahead, and with at most 168 VGPRs per wavefront three workgroups share a
 // CU (three wavefronts per SIMD): their barriers are independent, so one's
 // softmax, LDS reads and DMA waits overlap the others' MFMAs.  At B = 64
-// (two-wavefront workgroups) two buffers suffice and LDS bounds the
-// occupancy instead of registers.
+// (two-wavefront workgroups) the kernel needs more than 170 VGPRs, so two
+// wavefronts per SIMD (four workgroups per CU) is the register bound; two
+// stage buffers (32 KiB at d = 128) fit four workgroups, three would leave
+// LDS for only three.
 //
 // K and V stages are row-major with an XOR swizzle of the 16-byte chunks:
 // K operand reads (ds_read_b128 of one key row) and V operand reads
@@ -115,7 +117,8 @@ constexpr int kStageKeys = 32;   // keys per LDS stage
 
 // Stage buffers: 3 (DMA two stages ahead, 48 KiB at d = 128) for B = 128,
 // where three 4-wavefront workgroups then share a CU; 2 for B = 64, where
-// the 2-wavefront workgroups are limited by LDS rather than registers.
+// registers allow four 2-wavefront workgroups per CU and three buffers
+// would leave LDS for only three.
 template <int B>
 constexpr int stage_bufs() { return B == 128 ? 3 : 2; }
 
