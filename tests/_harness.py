@@ -36,7 +36,7 @@ def upload(x: syn.Inputs, device="cuda"):
     return tuple(torch.from_numpy(a).to(device) for a in (x.q, x.k, x.v))
 
 
-class GpuRun:
+class DeviceRun:
     """Plan, upload and run the whole path once; keep host copies."""
 
     def __init__(self, w: syn.Workload, x: syn.Inputs = None, out_dtype="f32", vnorm_mode=0,
@@ -98,7 +98,7 @@ def check_scores(got: np.ndarray, ref: np.ndarray, dtype: str, what: str,
     return float(err.max()), float(rel.max())
 
 
-def select_rows_crossfed(r: GpuRun, rows):
+def select_rows_crossfed(r: DeviceRun, rows):
     """Oracle selection on the GPU's own scores must equal the GPU's lists."""
     offs, _ = O.score_offsets(r.cu_blocks)
     seq_of = np.repeat(np.arange(len(r.cu_blocks) - 1), np.diff(r.cu_blocks))
@@ -115,7 +115,7 @@ def select_rows_crossfed(r: GpuRun, rows):
         assert np.all(r.idx[h, b, n:] == -1), (h, b)
 
 
-def attn_rows_crossfed(r: GpuRun, rows, what="attn"):
+def attn_rows_crossfed(r: DeviceRun, rows, what="attn"):
     """Oracle attention with the GPU's block lists, on sampled rows."""
     res = O.sparse_attn(r.x.q, r.x.k, r.x.v, r.idx, r.count, r.w.cu_seqlens, r.w.block,
                         rows=rows)
@@ -134,11 +134,11 @@ def attn_rows_crossfed(r: GpuRun, rows, what="attn"):
     return worst, lse_worst
 
 
-def all_rows(r: GpuRun):
+def all_rows(r: DeviceRun):
     return [(h, b) for h in range(r.w.num_q_heads) for b in range(int(r.cu_blocks[-1]))]
 
 
-def sample_rows(r: GpuRun, n: int, seed: int = 0):
+def sample_rows(r: DeviceRun, n: int, seed: int = 0):
     """First, last and diagonal-interesting rows plus a random sample."""
     rng = np.random.default_rng(seed)
     nbT = int(r.cu_blocks[-1])

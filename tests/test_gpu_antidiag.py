@@ -57,7 +57,7 @@ CASES = [("b64-d128-varlen", 1), ("b64-d128-varlen", 4), ("b64-d128-varlen", 64)
 
 def _check(w, stride, n_attn_rows=24):
     H.log(f"case antidiag {w.name} stride {stride} metric {w.metric}")
-    r = H.GpuRun(w, score_stride=stride)
+    r = H.DeviceRun(w, score_stride=stride)
     wv = O.pool_vnorm(r.x.v, w.cu_seqlens, w.block)
     ref = O.score_antidiag(r.x.q, r.x.k, wv, w.cu_seqlens, w.block, stride, w.metric, w.beta)
     fin = np.isfinite(ref)
@@ -126,7 +126,7 @@ def test_antidiag_rejects_bad_arguments():
 
 def _full_size_rows(w, stride, n_rows, seed):
     H.log(f"case antidiag full-size {w.name} stride {stride}: generating inputs")
-    r = H.GpuRun(w, out_dtype="bf16", score_stride=stride)
+    r = H.DeviceRun(w, out_dtype="bf16", score_stride=stride)
     H.log("  GPU done; metric rows (sampled)")
     wv = O.pool_vnorm(r.x.v, w.cu_seqlens, w.block)
     offs, _ = O.score_offsets(r.cu_blocks)
@@ -163,7 +163,7 @@ def test_antidiag_full_size_128k():
     w = syn.WORKLOADS["llama3-8b-128k-b128"]
     stride = 16
     H.log(f"case antidiag full-size {w.name} stride {stride}: generating inputs")
-    r = H.GpuRun(w, out_dtype="bf16", score_stride=stride)
+    r = H.DeviceRun(w, out_dtype="bf16", score_stride=stride)
     H.log("  GPU done; metric rows (sampled)")
     wv = O.pool_vnorm(r.x.v, w.cu_seqlens, w.block)
     offs, _ = O.score_offsets(r.cu_blocks)

@@ -45,7 +45,7 @@ SMALL = {
 }
 
 
-def _full_check(r: H.GpuRun):
+def _full_check(r: H.DeviceRun):
     w = r.w
     ref = O.prefill(r.x.q, r.x.k, r.x.v, w.cu_seqlens, w.block, w.sink_blocks, w.k_min,
                     w.rho0, w.tau, metric=w.metric, beta=w.beta, budget_mode=w.budget_mode,
@@ -84,14 +84,14 @@ def _full_check(r: H.GpuRun):
 def test_small_workload_every_stage(name):
     _cuda()
     H.log(f"case {name}")
-    _full_check(H.GpuRun(SMALL[name]))
+    _full_check(H.DeviceRun(SMALL[name]))
 
 
 @pytest.mark.parametrize("name", ["bf16-b64-d128-varlen-ragged", "bf16-b128-d128-gqa4"])
 def test_bf16_output_mode(name):
     _cuda()
     H.log(f"case {name} bf16 out")
-    r = H.GpuRun(SMALL[name], out_dtype="bf16")
+    r = H.DeviceRun(SMALL[name], out_dtype="bf16")
     rows = H.all_rows(r)
     H.attn_rows_crossfed(r, rows, "bf16-out")
 
@@ -122,20 +122,20 @@ MODES = {
 def test_metric_and_budget_modes_every_stage(name):
     _cuda()
     H.log(f"case mode {name}")
-    _full_check(H.GpuRun(MODES[name]))
+    _full_check(H.DeviceRun(MODES[name]))
 
 
 def test_single_head_1k_fp32_workload():
     _cuda()
     w = syn.WORKLOADS["single-head-1k-fp32"]
     H.log("case single-head-1k-fp32")
-    _full_check(H.GpuRun(w))
+    _full_check(H.DeviceRun(w))
 
 
 def test_vnorm_max_mode():
     _cuda()
     w = SMALL["bf16-b64-d128-varlen-ragged"]
-    r = H.GpuRun(w, vnorm_mode=stem.STEM_VNORM_MAX)
+    r = H.DeviceRun(w, vnorm_mode=stem.STEM_VNORM_MAX)
     np.testing.assert_allclose(r.vnorm, O.pool_vnorm(r.x.v, w.cu_seqlens, w.block, "max"),
                                rtol=1e-5, atol=1e-5)
 
@@ -146,7 +146,7 @@ def test_full_budget_equals_dense_causal(dtype, B, d):
     _cuda()
     w = syn.custom([700, 1200], 4, 2, d, dtype, B, sink_blocks=1, k_min=10 ** 6, rho0=0.0,
                    tau=1.0, seed=21)
-    r = H.GpuRun(w)
+    r = H.DeviceRun(w)
     assert np.all(r.count == np.concatenate([np.arange(1, n + 1) for n in np.diff(r.cu_blocks)]))
     o, lse = O.dense_causal_attn(r.x.q, r.x.k, r.x.v, w.cu_seqlens)
     H.check_out(r.out, o, dtype, "f32", "dense")
@@ -163,7 +163,7 @@ def test_many_short_sequences():
     w = syn.custom(lens, 4, 2, 128, "bf16", 64, sink_blocks=2, k_min=1, rho0=0.7, tau=2.0,
                    seed=44).replace(name="many-sequences")
     H.log("case many short sequences")
-    _full_check(H.GpuRun(w))
+    _full_check(H.DeviceRun(w))
 
 
 def test_edge_shapes():
@@ -175,7 +175,7 @@ def test_edge_shapes():
         w = syn.custom(seqlens, 4, 2, 128, "bf16", 64, sink_blocks=S, k_min=kmin, rho0=rho0,
                        tau=2.0, seed=31)
         H.log(f"case edge {seqlens} S={S} k_min={kmin}")
-        _full_check(H.GpuRun(w))
+        _full_check(H.DeviceRun(w))
 
 
 def test_equal_scores_pick_smallest_blocks():
@@ -187,7 +187,7 @@ def test_equal_scores_pick_smallest_blocks():
     one = syn.bf16_bits(np.ones(1, np.float32))[0]
     x.k_bits[:] = one; x.v_bits[:] = one
     x.k[:] = 1.0; x.v[:] = 1.0
-    r = H.GpuRun(w, x=x)
+    r = H.DeviceRun(w, x=x)
     for h in range(2):
         for i in range(40):
             # k_i = min(i + 1, 2 + 1 + 5): the 5 free slots go to blocks 2..6
@@ -204,14 +204,14 @@ def test_select_long_budget_and_wide_ties():
     w = syn.custom([64 * 300], 2, 1, 128, "bf16", 64, sink_blocks=2, k_min=100, rho0=0.0,
                    tau=1.0, seed=51)
     H.log("case select k_min=100")
-    _full_check(H.GpuRun(w))
+    _full_check(H.DeviceRun(w))
     w = syn.custom([64 * 200], 2, 1, 128, "bf16", 64, sink_blocks=2, k_min=5, rho0=0.0, tau=1.0)
     x = syn.generate(w)
     one = syn.bf16_bits(np.ones(1, np.float32))[0]
     x.k_bits[:] = one; x.v_bits[:] = one
     x.k[:] = 1.0; x.v[:] = 1.0
     H.log("case select 200 tied blocks")
-    r = H.GpuRun(w, x=x)
+    r = H.DeviceRun(w, x=x)
     for h in range(2):
         for i in range(200):
             want = list(range(i + 1)) if i < 8 else list(range(7)) + [i]
@@ -226,7 +226,7 @@ def _full_size(name, n_attn_rows: int, **params):
     w = (syn.WORKLOADS[name] if isinstance(name, str) else name).replace(**params)
     name = w.name
     H.log(f"case full-size {name}: generating inputs")
-    r = H.GpuRun(w, out_dtype="bf16")
+    r = H.DeviceRun(w, out_dtype="bf16")
     H.log(f"case full-size {name}: GPU done, checking pooled values")
     t = H.TOL[w.dtype]
     np.testing.assert_allclose(r.qbar, O.pool_mean(r.x.q, w.cu_seqlens, w.block),
