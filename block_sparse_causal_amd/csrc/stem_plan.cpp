@@ -25,13 +25,16 @@ int64_t tri(int64_t n) { return n * (n + 1) / 2; }
 // precision with the C library exp and ceil; every product and sum is its
 // own statement so that no fused multiply-add changes the rounding.
 double kdyn_raw(int64_t i, int64_t nb, const stem_params &p) {
-  if (p.budget_mode == STEM_BUDGET_LINEAR) {
+  if (p.budget_mode == STEM_BUDGET_LINEAR || p.budget_mode == STEM_BUDGET_LINEAR_FRACTION) {
     const double f = nb <= 1 ? 0.0 : static_cast<double>(i) / static_cast<double>(nb - 1);
     const double a = p.k_start * (1.0 - f);
     const double b = p.mu * p.k_start;
     const double c = b * f;
     const double x = a + c;
-    return std::ceil(x);
+    if (p.budget_mode == STEM_BUDGET_LINEAR) return std::ceil(x);
+    // a share of the row's i + 1 causal key blocks
+    const double y = x * static_cast<double>(i + 1);
+    return std::ceil(y);
   }
   const double e = std::exp(-static_cast<double>(i) / p.tau);
   const double x = p.rho0 * e * static_cast<double>(i + 1);
@@ -72,6 +75,9 @@ extern "C" int stem_plan(const stem_problem *pr, const stem_params *pa,
     if (!std::isfinite(pa->tau) || !(pa->tau > 0.0)) return STEM_EINVAL;
   } else if (pa->budget_mode == STEM_BUDGET_LINEAR) {
     if (!std::isfinite(pa->k_start) || pa->k_start < 0.0) return STEM_EINVAL;
+    if (!(pa->mu >= 0.0 && pa->mu <= 1.0)) return STEM_EINVAL;
+  } else if (pa->budget_mode == STEM_BUDGET_LINEAR_FRACTION) {
+    if (!(pa->k_start >= 0.0 && pa->k_start <= 1.0)) return STEM_EINVAL;
     if (!(pa->mu >= 0.0 && pa->mu <= 1.0)) return STEM_EINVAL;
   } else {
     return STEM_EINVAL;

@@ -20,9 +20,10 @@ _lib = None
 STEM_OK, STEM_EINVAL, STEM_EUNSUPPORTED, STEM_EHIP, STEM_ESPACE = 0, -1, -2, -3, -4
 STEM_F32, STEM_BF16 = 0, 1
 STEM_VNORM_MEAN, STEM_VNORM_MAX = 0, 1
-STEM_BUDGET_EXP, STEM_BUDGET_LINEAR = 0, 1
+STEM_BUDGET_EXP, STEM_BUDGET_LINEAR, STEM_BUDGET_LINEAR_FRACTION = 0, 1, 2
 STEM_METRIC_OUTPUT_AWARE, STEM_METRIC_ADDITIVE, STEM_METRIC_ROUTING = 0, 1, 2
-BUDGET_MODES = {"exp": STEM_BUDGET_EXP, "linear": STEM_BUDGET_LINEAR}
+BUDGET_MODES = {"exp": STEM_BUDGET_EXP, "linear": STEM_BUDGET_LINEAR,
+                "linear_fraction": STEM_BUDGET_LINEAR_FRACTION}
 METRICS = {"output_aware": STEM_METRIC_OUTPUT_AWARE, "additive": STEM_METRIC_ADDITIVE,
            "routing": STEM_METRIC_ROUTING}
 STEM_PLAN_MAGIC = 0x5354454D
@@ -188,7 +189,7 @@ class Plan:
 def stem_plan(cu_seqlens: Sequence[int], num_q_heads: int, num_kv_heads: int, head_dim: int,
               block: int, dtype: str, sink_blocks: int, k_min: int, rho0: float,
               tau: float, budget_mode: str = "exp", k_start: float = 0.0, mu: float = 0.0,
-              metric: str = "output_aware", beta: float = 0.5) -> Plan:
+              metric: str = "output_aware", beta: float = 0.2) -> Plan:
     cu = np.ascontiguousarray(np.asarray(cu_seqlens, dtype=np.int32))
     pr = stem_problem(len(cu) - 1, cu.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
                       num_q_heads, num_kv_heads, head_dim, block, DTYPES.get(dtype, 99))

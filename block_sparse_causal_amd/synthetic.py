@@ -50,11 +50,11 @@ class Workload:
     rho0: float
     tau: float            # decay length, in blocks
     seed: int = 0
-    budget_mode: str = "exp"          # "exp" (rho0, tau) or "linear" (k_start, mu)
+    budget_mode: str = "exp"          # "exp" (rho0, tau), "linear" or "linear_fraction" (k_start, mu)
     k_start: float = 0.0              # linear budget: dynamic blocks at the first row
     mu: float = 0.0                   # linear budget: k_end / k_start
     metric: str = "output_aware"      # "output_aware", "additive" or "routing"
-    beta: float = 0.5                 # additive metric weight
+    beta: float = 0.2                 # additive metric weight (the pages' value)
 
     @property
     def total_tokens(self) -> int:

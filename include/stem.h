@@ -55,7 +55,12 @@ typedef enum {
 typedef enum { STEM_F32 = 0, STEM_BF16 = 1 } stem_dtype;
 
 /* Shape of the position-dependent budget (see stem_params). */
-typedef enum { STEM_BUDGET_EXP = 0, STEM_BUDGET_LINEAR = 1 } stem_budget_mode;
+typedef enum {
+  STEM_BUDGET_EXP = 0,              /* exponential decay (rho0, tau)                   */
+  STEM_BUDGET_LINEAR = 1,           /* linear k_start -> mu * k_start, k_start in blocks */
+  STEM_BUDGET_LINEAR_FRACTION = 2   /* the same ramp, k_start a fraction of the causal
+                                       blocks of each query block                      */
+} stem_budget_mode;
 
 /* Which block metric stem_score writes (see stem_score). */
 typedef enum {
@@ -88,7 +93,10 @@ typedef struct stem_problem {
  *   STEM_BUDGET_LINEAR (the gist.science pages' linear interpolation from
  *   k_start to k_end = mu * k_start over the sequence's query blocks):
  *     max(k_min, ceil(k_start * (1 - f) + mu * k_start * f)), f = i / (nb - 1)
- * evaluated in fp64, and the kept count is
+ *   STEM_BUDGET_LINEAR_FRACTION (the same ramp read as a share of the causal
+ *   blocks: row i keeps that fraction of its i + 1 key blocks):
+ *     max(k_min, ceil((k_start * (1 - f) + mu * k_start * f) * (i + 1)))
+ * evaluated in fp64 (f = 0 when nb = 1), and the kept count is
  *   k_i = i + 1                                if i < sink_blocks
  *       = min(i + 1, sink_blocks + 1 + k_dyn(i)) otherwise
  * so the first sink_blocks blocks (initial tokens are the anchors every
@@ -102,8 +110,9 @@ typedef struct stem_params {
   double tau;                   /* > 0, in blocks (EXP) */
   int32_t budget_mode;          /* stem_budget_mode */
   int32_t metric_mode;          /* stem_metric_mode */
-  double k_start;               /* >= 0, finite (LINEAR), in blocks */
-  double mu;                    /* in [0, 1] (LINEAR) */
+  double k_start;               /* LINEAR: >= 0, finite, in blocks;
+                                   LINEAR_FRACTION: in [0, 1], a fraction */
+  double mu;                    /* in [0, 1] (LINEAR, LINEAR_FRACTION) */
   double beta;                  /* >= 0, finite (ADDITIVE metric) */
 } stem_params;
 

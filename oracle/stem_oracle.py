@@ -137,7 +137,7 @@ METRICS = ("output_aware", "additive", "routing")
 
 def score(qbar: np.ndarray, kbar: np.ndarray, w: np.ndarray,
           cu_blocks: np.ndarray, head_dim: int, metric: str = "output_aware",
-          beta: float = 0.5) -> np.ndarray:
+          beta: float = 0.2) -> np.ndarray:
     """Packed lower-triangular metric m [Hq, tri_total] (float64).
 
     For query head h (KV head g = h // (Hq/Hkv)), sequence s and local query
@@ -146,7 +146,9 @@ def score(qbar: np.ndarray, kbar: np.ndarray, w: np.ndarray,
         p_ij = exp(s_ij - max_j s) / sum_j exp(s_ij - max_j s)
         m_ij = p_ij * w_j                         metric "output_aware"
              = s_ij + beta * max(0, log(w_j^2))   metric "additive" (the
-               displayed formula of [es] 2.B and [fr] 2.B)
+               displayed formula of [es] 2.B and [fr] 2.B; beta defaults to
+               0.2, the value [nl] gives in its Output-Aware Metric paragraph
+               and [es] 3 reports as the ablation's best)
              = p_ij                               metric "routing" (attention
                score alone, the criterion [es] 1 argues against)
     """
@@ -166,7 +168,7 @@ def score(qbar: np.ndarray, kbar: np.ndarray, w: np.ndarray,
 
 def score_row_values(qbar: np.ndarray, kbar: np.ndarray, w: np.ndarray,
                      cu_blocks: np.ndarray, head_dim: int, h: int, s: int, i: int,
-                     metric: str = "output_aware", beta: float = 0.5) -> np.ndarray:
+                     metric: str = "output_aware", beta: float = 0.2) -> np.ndarray:
     """One row of the metric: m_i0 .. m_ii for query head h, sequence s,
     local query block i (see score)."""
     if metric not in METRICS:
@@ -178,7 +180,7 @@ def score_row_values(qbar: np.ndarray, kbar: np.ndarray, w: np.ndarray,
 
 
 def metric_from_logits(logits: np.ndarray, wj: np.ndarray, metric: str = "output_aware",
-                       beta: float = 0.5) -> np.ndarray:
+                       beta: float = 0.2) -> np.ndarray:
     """The metric of one row from its block logits s_i0 .. s_ii and the key
     blocks' V magnitudes (the three forms listed in score).  A row whose
     logits are all -inf (no sampled evidence, see antidiag_row_logits) gets
@@ -289,7 +291,7 @@ def antidiag_block_logits(q: np.ndarray, k: np.ndarray, cu_seqlens: Sequence[int
 
 def score_antidiag(q: np.ndarray, k: np.ndarray, w: np.ndarray, cu_seqlens: Sequence[int],
                    block: int, stride: int, metric: str = "output_aware",
-                   beta: float = 0.5) -> np.ndarray:
+                   beta: float = 0.2) -> np.ndarray:
     """The metric with anti-diagonal sampled block logits in place of the
     pooled ones: packed m [Hq, tri_total] (float64)."""
     cu_blocks = block_layout(cu_seqlens, block)
@@ -349,6 +351,29 @@ def budget_linear(nb: int, sink_blocks: int, k_min: int, k_start: float,
             continue
         frac = 0.0 if nb <= 1 else i / (nb - 1)
         kd = max(k_min, int(math.ceil(k_start * (1.0 - frac) + mu * k_start * frac)))
+        out[i] = min(i + 1, sink_blocks + 1 + kd)
+    return out
+
+
+def budget_linear_fraction(nb: int, sink_blocks: int, k_min: int, k_start: float,
+                           mu: float) -> np.ndarray:
+    """The linear ramp of [es] 2.A / [fr] 2.A read as a share of each row's
+    causal blocks (the pages give no unit for k_start): query block i keeps
+    the fraction r(i) = k_start at the sequence's first block decaying
+    linearly to mu*k_start at its last, of its i+1 key blocks, rounded up and
+    floored at k_min; sinks and diagonal on top, the causal count caps it:
+        f        = i / (nb - 1)            (0 when nb = 1)
+        r(i)     = k_start*(1-f) + mu*k_start*f
+        k_dyn(i) = max(k_min, ceil(r(i) * (i+1)))
+        k_i      = i+1 if i < S, else min(i+1, S + 1 + k_dyn(i))"""
+    out = np.zeros(nb, dtype=np.int64)
+    for i in range(nb):
+        if i < sink_blocks:
+            out[i] = i + 1
+            continue
+        frac = 0.0 if nb <= 1 else i / (nb - 1)
+        share = k_start * (1.0 - frac) + mu * k_start * frac
+        kd = max(k_min, int(math.ceil(share * (i + 1))))
         out[i] = min(i + 1, sink_blocks + 1 + kd)
     return out
 
@@ -514,7 +539,8 @@ def budgets_for(cu_blocks: np.ndarray, sink_blocks: int, k_min: int,
                 rho0: float, tau: float, mode: str = "exp", k_start: float = 0.0,
                 mu: float = 0.0) -> np.ndarray:
     """Per-global-block budget table, each sequence restarting at i = 0;
-    mode "exp" uses budget, mode "linear" uses budget_linear."""
+    mode "exp" uses budget, mode "linear" budget_linear and mode
+    "linear_fraction" budget_linear_fraction."""
     if mode == "exp":
         parts = [budget(int(cu_blocks[s + 1] - cu_blocks[s]), sink_blocks, k_min, rho0, tau)
                  for s in range(len(cu_blocks) - 1)]
@@ -522,13 +548,17 @@ def budgets_for(cu_blocks: np.ndarray, sink_blocks: int, k_min: int,
         parts = [budget_linear(int(cu_blocks[s + 1] - cu_blocks[s]), sink_blocks, k_min,
                                k_start, mu)
                  for s in range(len(cu_blocks) - 1)]
+    elif mode == "linear_fraction":
+        parts = [budget_linear_fraction(int(cu_blocks[s + 1] - cu_blocks[s]), sink_blocks,
+                                        k_min, k_start, mu)
+                 for s in range(len(cu_blocks) - 1)]
     else:
         raise ValueError(mode)
     return np.concatenate(parts) if parts else np.zeros(0, np.int64)
 
 
 def prefill(q, k, v, cu_seqlens, block, sink_blocks, k_min, rho0, tau,
-            vnorm_mode: str = "mean", metric: str = "output_aware", beta: float = 0.5,
+            vnorm_mode: str = "mean", metric: str = "output_aware", beta: float = 0.2,
             budget_mode: str = "exp", k_start: float = 0.0, mu: float = 0.0,
             score_stride: Optional[int] = None):
     """pool -> score -> budget -> select -> attention.  Returns a dict of

@@ -98,6 +98,40 @@ def check_scores(got: np.ndarray, ref: np.ndarray, dtype: str, what: str,
     return float(err.max()), float(rel.max())
 
 
+def near_tie(mx: float, my: float, dtype: str, metric: str = "output_aware") -> bool:
+    """Whether two oracle metric values are close enough for the GPU's f32
+    scores (each within score_rel of its reference, relative to max(|m|, 1)
+    for the additive metric, relative to |m| otherwise) to rank them the
+    other way round: |mx - my| <= score_rel * (|mx| + |my|)."""
+    rel = TOL[dtype]["score_rel"]
+    floor = 1.0 if metric == "additive" else 1e-30
+    return abs(mx - my) <= rel * (max(abs(mx), floor) + max(abs(my), floor))
+
+
+def selection_agreement(r: DeviceRun, ref_idx: np.ndarray, ref_m: np.ndarray, heads,
+                        what: str) -> int:
+    """End to end: rows where the oracle's own selection (from its fp64
+    metric) differs from the GPU's.  In such a row every block the GPU kept
+    and the oracle did not, and every block the oracle kept and the GPU did
+    not, must be a near-tie of the oracle metric.  Returns the number of
+    differing rows."""
+    offs, _ = O.score_offsets(r.cu_blocks)
+    seq_of = np.repeat(np.arange(len(r.cu_blocks) - 1), np.diff(r.cu_blocks))
+    gpu = r.idx[list(heads)]
+    differ = np.argwhere(np.any(ref_idx != gpu, axis=2))
+    for hh, b in differ:
+        s = int(seq_of[b]); i = b - int(r.cu_blocks[s])
+        m = ref_m[hh, int(offs[s]) + O.tri(i):][:i + 1]
+        a = set(gpu[hh, b]) - set(ref_idx[hh, b])
+        c = set(ref_idx[hh, b]) - set(gpu[hh, b])
+        assert len(a) == len(c), (what, hh, b)
+        for x in a:
+            for y in c:
+                assert near_tie(m[x], m[y], r.w.dtype, r.w.metric), \
+                    (what, int(hh), int(b), int(x), int(y), m[x], m[y])
+    return len(differ)
+
+
 def select_rows_crossfed(r: DeviceRun, rows):
     """Oracle selection on the GPU's own scores must equal the GPU's lists."""
     offs, _ = O.score_offsets(r.cu_blocks)

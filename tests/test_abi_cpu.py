@@ -110,6 +110,23 @@ def test_plan_linear_budget_random_parameters(seed):
         p.budget, O.budgets_for(cub, S, k_min, 0.0, 1.0, "linear", k_start, mu))
 
 
+@pytest.mark.parametrize("seed", range(20))
+def test_plan_linear_fraction_budget_random_parameters(seed):
+    r = np.random.default_rng(300 + seed)
+    seqlens = list(r.integers(0, 4000, size=r.integers(1, 5)))
+    block = int(r.choice([64, 128]))
+    S = int(r.integers(0, 5))
+    k_min = int(r.integers(0, 6))
+    k_start = float(r.choice([r.uniform(0, 1), 0.25, 0.0, 1.0]))
+    mu = float(r.choice([r.uniform(0, 1), 0.0, 1.0, 0.7]))
+    cu = np.concatenate([[0], np.cumsum(seqlens)])
+    p = stem.stem_plan(cu, 4, 2, 64, block, "bf16", S, k_min, 0.0, 1.0,
+                       budget_mode="linear_fraction", k_start=k_start, mu=mu)
+    cub = O.block_layout(cu, block)
+    np.testing.assert_array_equal(
+        p.budget, O.budgets_for(cub, S, k_min, 0.0, 1.0, "linear_fraction", k_start, mu))
+
+
 def test_plan_carries_metric_mode_and_beta():
     for name, code in stem.METRICS.items():
         p = stem.stem_plan([0, 512], 2, 1, 64, 64, "f32", 1, 1, 0.5, 4.0, metric=name,
@@ -164,6 +181,11 @@ def test_plan_rejects_bad_arguments():
     assert bad(budget_mode="linear", k_start=float("inf")) == stem.STEM_EINVAL
     assert bad(budget_mode="linear", k_start=4.0, mu=1.5) == stem.STEM_EINVAL
     assert bad(budget_mode="linear", k_start=4.0, mu=float("nan")) == stem.STEM_EINVAL
+    # a fraction of the causal blocks lies in [0, 1]
+    assert bad(budget_mode="linear_fraction", k_start=1.5, mu=0.5) == stem.STEM_EINVAL
+    assert bad(budget_mode="linear_fraction", k_start=-0.1, mu=0.5) == stem.STEM_EINVAL
+    assert bad(budget_mode="linear_fraction", k_start=float("nan"), mu=0.5) == stem.STEM_EINVAL
+    assert bad(budget_mode="linear_fraction", k_start=0.5, mu=2.0) == stem.STEM_EINVAL
     # the exponential parameters are not checked in linear mode, and vice versa
     assert stem.stem_plan(*dict(ok, tau=0.0).values(), budget_mode="linear", k_start=2.0,
                           mu=0.5).info.kmax >= 1

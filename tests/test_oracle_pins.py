@@ -294,6 +294,45 @@ def test_budget_linear_special_cases():
                                                      O.budget_linear(30, 2, 1, 8, 0.25)]))
 
 
+def test_budget_linear_fraction_hand_table():
+    # nb = 5, S = 1, k_min = 0, k_start = 0.5, mu = 0.5: f = i/4, share
+    # r = 0.5(1 - f) + 0.25 f; k_dyn = ceil(r (i+1)): i=1 -> ceil(0.875) = 1,
+    # i=2 -> ceil(1.125) = 2, i=3 -> ceil(1.25) = 2, i=4 -> ceil(1.25) = 2;
+    # k_i = min(i+1, 1 + 1 + k_dyn)
+    assert list(O.budget_linear_fraction(5, 1, 0, 0.5, 0.5)) == [1, 2, 3, 4, 4]
+
+
+def test_budget_linear_fraction_special_cases():
+    # the whole causal row at every block: dense causal attention
+    assert list(O.budget_linear_fraction(40, 2, 0, 1.0, 1.0)) == list(range(1, 41))
+    # a zero share leaves the floor k_min
+    assert list(O.budget_linear_fraction(30, 1, 3, 0.0, 0.5)) == \
+        [1] + [min(i + 1, 1 + 1 + 3) for i in range(1, 30)]
+    # mu = 1: a constant share, ceil(r (i+1)) blocks, here r = 1/4
+    b = O.budget_linear_fraction(64, 0, 0, 0.25, 1.0)
+    assert list(b) == [min(i + 1, 1 + math.ceil(0.25 * (i + 1))) for i in range(64)]
+    # mu = 0: the share reaches zero at the last block
+    b = O.budget_linear_fraction(33, 0, 2, 0.5, 0.0)
+    assert b[32] == 1 + 2 and b[16] == 1 + math.ceil(0.25 * 17)
+    # one block: f = 0
+    assert list(O.budget_linear_fraction(1, 0, 0, 0.3, 0.5)) == [1]
+    # the per-sequence table restarts at every sequence
+    cub = np.array([0, 7, 7, 40])
+    t = O.budgets_for(cub, 2, 1, 0.0, 1.0, mode="linear_fraction", k_start=0.4, mu=0.7)
+    np.testing.assert_array_equal(
+        t, np.concatenate([O.budget_linear_fraction(7, 2, 1, 0.4, 0.7),
+                           O.budget_linear_fraction(33, 2, 1, 0.4, 0.7)]))
+
+
+def test_additive_metric_beta_default_is_the_pages_value():
+    import inspect
+    from block_sparse_causal_amd import synthetic as syn
+    beta = pages_parameters()["beta"]
+    for fn in (O.score, O.score_row_values, O.metric_from_logits, O.score_antidiag, O.prefill):
+        assert inspect.signature(fn).parameters["beta"].default == beta, fn.__name__
+    assert syn.custom([64], 1, 1, 64, "bf16", 64).beta == beta
+
+
 # ---------------------------------------------------------------- selection
 
 
