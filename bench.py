@@ -21,7 +21,10 @@ Reported (one JSON line on stdout, progress on stderr):
               operands and its streaming HBM read rate, re-measured by the
               library's probe kernels (the published peaks assume neither
               the power limit nor the memory system's efficiency)
-  cpu_baseline  the CPU oracle timed on a bounded sample and scaled up
+  cpu_baseline  the CPU oracle timed stage by stage on a bounded sample and
+              scaled up (fp64, the oracle's precision, plus an fp32 line)
+  step_ms_spread / attn_ms_spread  mean, median, min and max of the timed
+              steps (value is the mean)
 """
 from __future__ import annotations
 
@@ -163,7 +166,8 @@ def dense_attention_ms(w, q, k, v, reps: int):
 def cpu_baseline(w, x):
     """Time the oracle, as it stands, on one KV-head group (KV head 0 and its
     G query heads: pooling, every metric, selection and attention row of
-    those heads) and scale to all KV heads."""
+    those heads), stage by stage, and scale to all KV heads.  The oracle
+    computes in fp64; a second line runs the same code in fp32."""
     from oracle import stem_oracle as O
     try:
         from threadpoolctl import threadpool_info
@@ -172,16 +176,43 @@ def cpu_baseline(w, x):
         blas_threads = 1
     G = w.num_q_heads // w.num_kv_heads
     q, k, v = x.q[:, :G], x.k[:, :1], x.v[:, :1]
-    t = time.perf_counter()
-    res = O.prefill(q, k, v, w.cu_seqlens, w.block, w.sink_blocks, w.k_min, w.rho0, w.tau)
-    sec = time.perf_counter() - t
-    nbT = int(res["cu_blocks"][-1])
+    cu, B = w.cu_seqlens, w.block
+
+    def run(dt):
+        st = {}
+        t = time.perf_counter()
+        cub = O.block_layout(cu, B)
+        qbar = O.pool_mean(q, cu, B, dt)
+        kbar = O.pool_mean(k, cu, B, dt)
+        wv = O.pool_vnorm(v, cu, B, "mean", dt)
+        st["pool"] = time.perf_counter() - t
+        t = time.perf_counter()
+        m = O.score(qbar, kbar, wv, cub, w.head_dim, w.metric, w.beta, dt)
+        st["score"] = time.perf_counter() - t
+        t = time.perf_counter()
+        bud = O.budgets_for(cub, w.sink_blocks, w.k_min, w.rho0, w.tau, w.budget_mode,
+                            w.k_start, w.mu)
+        idx, cnt = O.select(m, cub, bud, w.sink_blocks)
+        st["budget_select"] = time.perf_counter() - t
+        t = time.perf_counter()
+        O.sparse_attn(q, k, v, idx, cnt, cu, B, dtype=dt)
+        st["attn"] = time.perf_counter() - t
+        return st
+
+    f64 = run(np.float64)
+    f32 = run(np.float32)
+    scale = w.num_kv_heads * 1e3
+    nbT = int(O.block_layout(cu, B)[-1])
     sample = (f"oracle prefill of KV head 0 and its {G} query heads of {w.name} "
               f"(pool, metric, budget, selection and attention of all {nbT} query blocks), "
               f"scaled by {w.num_kv_heads} KV heads")
-    return dict(value=round(sec * w.num_kv_heads * 1e3, 1), unit="ms", cores=int(blas_threads),
-                kind="oracle", sample=sample, sample_seconds=round(sec, 2),
-                host_cpus=len(os.sched_getaffinity(0)))
+    return dict(value=round(sum(f64.values()) * scale, 1), unit="ms", cores=int(blas_threads),
+                kind="oracle", sample=sample, sample_seconds=round(sum(f64.values()), 2),
+                host_cpus=len(os.sched_getaffinity(0)), precision="fp64",
+                stages_ms={k_: round(v_ * scale, 1) for k_, v_ in f64.items()},
+                fp32={"value": round(sum(f32.values()) * scale, 1), "unit": "ms",
+                      "stages_ms": {k_: round(v_ * scale, 1) for k_, v_ in f32.items()},
+                      "sample_seconds": round(sum(f32.values()), 2)})
 
 
 def measure_ceilings(reps: int = 5):
@@ -331,8 +362,10 @@ def main():
     names = ["pool", "score", "select", "attn"]
     stage_ms = {n: float(np.mean(s)) for n, s in zip(names, stage)}
     step_ms = float(np.mean(total))
-    log(f"step {step_ms:.3f} ms (wall {wall_ms:.3f} ms): " +
-        ", ".join(f"{n} {stage_ms[n]:.3f}" for n in names))
+    spread = lambda v: {"mean": round(float(np.mean(v)), 4), "median": round(float(np.median(v)), 4),
+                        "min": round(float(np.min(v)), 4), "max": round(float(np.max(v)), 4)}
+    log(f"step {step_ms:.3f} ms (median {np.median(total):.3f}, min {np.min(total):.3f}; "
+        f"wall {wall_ms:.3f} ms): " + ", ".join(f"{n} {stage_ms[n]:.3f}" for n in names))
 
     flops_alg = attn_flops(plan, diag_half=True)
     flops_full = attn_flops(plan, diag_half=False)
@@ -377,6 +410,8 @@ def main():
                      "flop_per_launch": flops_alg,
                      "avg_launch_ms": round(attn_ms, 4)},
         "stages_ms": {n: round(stage_ms[n], 4) for n in names},
+        "step_ms_spread": spread(total),
+        "attn_ms_spread": spread(stage[3]),
         "effective_tflops": {"attn_diag_half": round(achieved, 2),
                              "attn_full_tiles": round(flops_full / (attn_ms * 1e-3) / 1e12, 2),
                              "step_diag_half": round(flops_alg / (step_ms * 1e-3) / 1e12, 2)},

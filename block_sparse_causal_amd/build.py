@@ -32,13 +32,33 @@ def sources():
         sorted(glob.glob(os.path.join(CSRC, "*.cpp")))
 
 
-def build(verbose: bool = False, extra_flags=None) -> str:
-    """Compile every source into libstem.so (always recompiles)."""
-    tmp = LIB + ".tmp"
-    cmd = [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
-           "-Wall", "-Wno-unused-function",
+# Host-side AddressSanitizer and UndefinedBehaviorSanitizer for the host code
+# (planning, argument checks); every flag goes to the host compilation only,
+# the GPU code is built as usual.  The resulting library expects the ASan
+# runtime to be preloaded (see sanitizer_runtime).
+SANITIZE_HOST = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                 "-Xarch_host", "-fno-sanitize-recover=undefined",
+                 "-Xarch_host", "-fno-omit-frame-pointer", "-Xarch_host", "-g"]
+
+
+def sanitizer_runtime() -> str:
+    """Path of the clang ASan runtime matching hipcc (preloaded into the
+    process that loads a sanitized library)."""
+    out = subprocess.run([hipcc(), "-print-file-name=libclang_rt.asan-x86_64.so"],
+                         stdout=subprocess.PIPE, stderr=subprocess.DEVNULL, text=True).stdout.strip()
+    return out
+
+
+def build(verbose: bool = False, extra_flags=None, out: str = None, sanitize: bool = False) -> str:
+    """Compile every source into libstem.so (always recompiles); ``out``
+    builds elsewhere, ``sanitize`` adds the host sanitizers."""
+    lib = out or LIB
+    tmp = lib + ".tmp"
+    flags = list(extra_flags or []) + (SANITIZE_HOST if sanitize else [])
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
+           "-shared", "-Wall", "-Wno-unused-function",
            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-           f"-I{INCLUDE}", f"-I{CSRC}", "-o", tmp] + list(extra_flags or []) + sources()
+           f"-I{INCLUDE}", f"-I{CSRC}", "-o", tmp] + flags + sources()
     if verbose:
         print(" ".join(cmd), flush=True)
     proc = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
@@ -50,8 +70,8 @@ def build(verbose: bool = False, extra_flags=None) -> str:
         raise RuntimeError("hipcc failed:\n" + "\n".join(lines))
     if verbose and lines:
         print("\n".join(lines))
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
 
 
 if __name__ == "__main__":

@@ -174,7 +174,9 @@ extern "C" int stem_plan(const stem_problem *pr, const stem_params *pa,
     p_tri[s + 1] = t;
   }
   p_cu[ns] = cu[ns];
-  std::memcpy(p_bud, budget.data(), sizeof(int32_t) * budget.size());
+  // (an empty vector may hand out a null data pointer, which memcpy must
+  // not receive even for zero bytes)
+  if (!budget.empty()) std::memcpy(p_bud, budget.data(), sizeof(int32_t) * budget.size());
   // attention work order: most kept blocks first (longest-job-first keeps
   // the tail of the grid short); a final partial block counts as less work.
   std::vector<int32_t> order(static_cast<size_t>(nbT));
@@ -188,7 +190,7 @@ extern "C" int stem_plan(const stem_problem *pr, const stem_params *pa,
   };
   std::stable_sort(order.begin(), order.end(),
                    [&](int32_t x, int32_t y) { return cost(x) > cost(y); });
-  std::memcpy(p_ord, order.data(), sizeof(int32_t) * order.size());
+  if (!order.empty()) std::memcpy(p_ord, order.data(), sizeof(int32_t) * order.size());
   return STEM_OK;
 }
 

@@ -84,39 +84,41 @@ def score_offsets(cu_blocks: np.ndarray) -> Tuple[np.ndarray, int]:
 # step 1, [it] 2.C, [fr] 2.C step 1)
 
 
-def pool_mean(x: np.ndarray, cu_seqlens: Sequence[int], block: int) -> np.ndarray:
-    """Block mean of x [T, H, d] -> [H, nbT, d] (float64).
+def pool_mean(x: np.ndarray, cu_seqlens: Sequence[int], block: int,
+              dtype=np.float64) -> np.ndarray:
+    """Block mean of x [T, H, d] -> [H, nbT, d] (float64; ``dtype`` only
+    selects the precision of a timing run of the baseline)
 
     Block j of sequence s covers its tokens [j*B, min((j+1)*B, len_s)); the
     mean is over the tokens actually present."""
     cu = np.asarray(cu_seqlens, dtype=np.int64)
     cub = block_layout(cu, block)
     T, H, d = x.shape
-    out = np.zeros((H, int(cub[-1]), d), dtype=np.float64)
+    out = np.zeros((H, int(cub[-1]), d), dtype=dtype)
     for s in range(len(cu) - 1):
         a, e = int(cu[s]), int(cu[s + 1])
         for jl in range(int(cub[s + 1] - cub[s])):
             t0 = a + jl * block
             t1 = min(t0 + block, e)
-            seg = x[t0:t1].astype(np.float64)          # [n, H, d]
+            seg = x[t0:t1].astype(dtype)               # [n, H, d]
             out[:, int(cub[s]) + jl, :] = seg.sum(axis=0) / (t1 - t0)
     return out
 
 
 def pool_vnorm(v: np.ndarray, cu_seqlens: Sequence[int], block: int,
-               mode: str = "mean") -> np.ndarray:
+               mode: str = "mean", dtype=np.float64) -> np.ndarray:
     """Block V magnitude w [Hkv, nbT]: mean (default) or max over the block's
     tokens of the token's L2 norm ||v_t||_2."""
     cu = np.asarray(cu_seqlens, dtype=np.int64)
     cub = block_layout(cu, block)
     T, H, d = v.shape
-    out = np.zeros((H, int(cub[-1])), dtype=np.float64)
+    out = np.zeros((H, int(cub[-1])), dtype=dtype)
     for s in range(len(cu) - 1):
         a, e = int(cu[s]), int(cu[s + 1])
         for jl in range(int(cub[s + 1] - cub[s])):
             t0 = a + jl * block
             t1 = min(t0 + block, e)
-            seg = v[t0:t1].astype(np.float64)
+            seg = v[t0:t1].astype(dtype)
             norms = np.sqrt((seg * seg).sum(axis=2))   # [n, H]
             if mode == "mean":
                 out[:, int(cub[s]) + jl] = norms.sum(axis=0) / (t1 - t0)
@@ -137,8 +139,9 @@ METRICS = ("output_aware", "additive", "routing")
 
 def score(qbar: np.ndarray, kbar: np.ndarray, w: np.ndarray,
           cu_blocks: np.ndarray, head_dim: int, metric: str = "output_aware",
-          beta: float = 0.2) -> np.ndarray:
-    """Packed lower-triangular metric m [Hq, tri_total] (float64).
+          beta: float = 0.2, dtype=np.float64) -> np.ndarray:
+    """Packed lower-triangular metric m [Hq, tri_total] (float64; ``dtype``
+    as for pool_mean).
 
     For query head h (KV head g = h // (Hq/Hkv)), sequence s and local query
     block i, the row holds, for j = 0..i (local key blocks):
@@ -154,7 +157,7 @@ def score(qbar: np.ndarray, kbar: np.ndarray, w: np.ndarray,
     """
     Hq = qbar.shape[0]
     offs, total = score_offsets(cu_blocks)
-    out = np.zeros((Hq, total), dtype=np.float64)
+    out = np.zeros((Hq, total), dtype=dtype)
     for h in range(Hq):
         for s in range(len(cu_blocks) - 1):
             nb = int(cu_blocks[s + 1]) - int(cu_blocks[s])
@@ -162,33 +165,34 @@ def score(qbar: np.ndarray, kbar: np.ndarray, w: np.ndarray,
                 row0 = int(offs[s]) + tri(i)
                 out[h, row0:row0 + i + 1] = score_row_values(qbar, kbar, w, cu_blocks,
                                                              head_dim, h, s, i,
-                                                             metric, beta)
+                                                             metric, beta, dtype)
     return out
 
 
 def score_row_values(qbar: np.ndarray, kbar: np.ndarray, w: np.ndarray,
                      cu_blocks: np.ndarray, head_dim: int, h: int, s: int, i: int,
-                     metric: str = "output_aware", beta: float = 0.2) -> np.ndarray:
+                     metric: str = "output_aware", beta: float = 0.2,
+                     dtype=np.float64) -> np.ndarray:
     """One row of the metric: m_i0 .. m_ii for query head h, sequence s,
     local query block i (see score)."""
     if metric not in METRICS:
         raise ValueError(metric)
     g = h // (qbar.shape[0] // kbar.shape[0])
     b0 = int(cu_blocks[s])
-    logits = kbar[g, b0:b0 + i + 1, :] @ qbar[h, b0 + i, :] * (1.0 / math.sqrt(head_dim))
-    return metric_from_logits(logits, w[g, b0:b0 + i + 1], metric, beta)
+    logits = kbar[g, b0:b0 + i + 1, :] @ qbar[h, b0 + i, :] * dtype(1.0 / math.sqrt(head_dim))
+    return metric_from_logits(logits, w[g, b0:b0 + i + 1], metric, beta, dtype)
 
 
 def metric_from_logits(logits: np.ndarray, wj: np.ndarray, metric: str = "output_aware",
-                       beta: float = 0.2) -> np.ndarray:
+                       beta: float = 0.2, dtype=np.float64) -> np.ndarray:
     """The metric of one row from its block logits s_i0 .. s_ii and the key
     blocks' V magnitudes (the three forms listed in score).  A row whose
     logits are all -inf (no sampled evidence, see antidiag_row_logits) gets
     routing weight 0 everywhere."""
     if metric not in METRICS:
         raise ValueError(metric)
-    logits = np.asarray(logits, dtype=np.float64)
-    wj = np.asarray(wj, dtype=np.float64)
+    logits = np.asarray(logits, dtype=dtype)
+    wj = np.asarray(wj, dtype=dtype)
     if metric == "additive":
         # log(0) = -inf, so a block of zero values gets no bonus
         with np.errstate(divide="ignore"):
@@ -438,7 +442,7 @@ def select(m: np.ndarray, cu_blocks: np.ndarray, budgets: np.ndarray,
 
 
 def attn_row(q: np.ndarray, k: np.ndarray, v: np.ndarray, cu_seqlens, block: int,
-             s: int, i: int, h: int, G: int, blocks: Iterable[int]):
+             s: int, i: int, h: int, G: int, blocks: Iterable[int], dtype=np.float64):
     """Output rows and natural-log LSE for the tokens of query block i of
     sequence s, query head h, attending to the given local key blocks.
 
@@ -454,9 +458,9 @@ def attn_row(q: np.ndarray, k: np.ndarray, v: np.ndarray, cu_seqlens, block: int
         j0 = a + int(j) * block
         keys.extend(range(j0, min(j0 + block, e)))
     keys = np.asarray(keys, dtype=np.int64)
-    qi = q[t0:t1, h, :].astype(np.float64)
-    kj = k[keys, g, :].astype(np.float64)
-    vj = v[keys, g, :].astype(np.float64)
+    qi = q[t0:t1, h, :].astype(dtype)
+    kj = k[keys, g, :].astype(dtype)
+    vj = v[keys, g, :].astype(dtype)
     d = q.shape[2]
     logits = (qi @ kj.T) / math.sqrt(d)
     allowed = keys[None, :] <= np.arange(t0, t1)[:, None]
@@ -471,7 +475,7 @@ def attn_row(q: np.ndarray, k: np.ndarray, v: np.ndarray, cu_seqlens, block: int
 
 def sparse_attn(q: np.ndarray, k: np.ndarray, v: np.ndarray, idx: np.ndarray,
                 count: np.ndarray, cu_seqlens, block: int,
-                rows: Optional[Iterable[Tuple[int, int]]] = None):
+                rows: Optional[Iterable[Tuple[int, int]]] = None, dtype=np.float64):
     """Block-sparse causal attention.
 
     Returns (o [T, Hq, d], lse [Hq, T]) in float64 for every row when
@@ -487,12 +491,12 @@ def sparse_attn(q: np.ndarray, k: np.ndarray, v: np.ndarray, idx: np.ndarray,
         s = int(seq_of_block[b])
         i = b - int(cub[s])
         blocks = idx[h, b, :int(count[h, b])]
-        return attn_row(q, k, v, cu, block, s, i, h, G, blocks)
+        return attn_row(q, k, v, cu, block, s, i, h, G, blocks, dtype)
 
     if rows is not None:
         return {(h, b): one(h, b) for (h, b) in rows}
-    o = np.zeros((T, Hq, d), dtype=np.float64)
-    lse = np.zeros((Hq, T), dtype=np.float64)
+    o = np.zeros((T, Hq, d), dtype=dtype)
+    lse = np.zeros((Hq, T), dtype=dtype)
     for h in range(Hq):
         for b in range(int(cub[-1])):
             s = int(seq_of_block[b])
