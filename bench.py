@@ -328,6 +328,9 @@ def main():
                          "(stem_score_antidiag) instead of the pooled blocks")
     ap.add_argument("--no-ceilings", action="store_true",
                     help="skip the matrix-core and HBM probe kernels")
+    ap.add_argument("--tokens", type=int, default=None,
+                    help="one sequence of this many tokens with the workload's head shape and "
+                         "parameters (a point of the context-length sweep)")
     ap.add_argument("--sweep", action="store_true",
                     help="latency against context length (8K..128K), Stem vs dense")
     args = ap.parse_args()
@@ -346,6 +349,11 @@ def main():
         sweep(name, args.steps, args.warmup, args.dense_reps, args.score_stride)
         return
     w = syn.WORKLOADS[name]
+    if args.tokens:
+        w = w.replace(name=f"{name}@{args.tokens // 1024}k", seqlens=(args.tokens,),
+                      seed=w.seed + 100 + SWEEP_TOKENS.index(args.tokens)
+                      if args.tokens in SWEEP_TOKENS else w.seed + 200)
+        name = w.name
     log(f"workload {name}: generating seeded inputs")
     t = time.perf_counter()
     x = syn.generate(w)
