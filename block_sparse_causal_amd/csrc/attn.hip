@@ -25,7 +25,10 @@
 // L land on one XCD, and L enumerates (KV head, query block by decreasing
 // work, query head within the group): the query heads sharing a KV head and
 // the neighbouring rows (which keep mostly the same key blocks) then hit
-// the same L2.
+// the same L2.  With fewer than 8 KV heads (a divisor of 8), each KV head is
+// shared by 8 / Hkv XCDs that take its query blocks' ranks in turn, so that
+// every XCD gets the same mix of long and short rows (contiguous halves of
+// the work order would give one XCD the long rows and the other the short).
 #include <type_traits>
 
 #include "stem_device.h"
@@ -45,7 +48,8 @@ struct AttnArgs {
   int32_t Hq, Hkv, nbT, kmax;
   int64_t T;
   int32_t n_items;     // Hq * nbT
-  int32_t per_xcd;     // ceil(n_items / 8)
+  int32_t per_xcd;     // work items per XCD
+  int32_t split;       // XCDs sharing one KV head (1: contiguous ranges)
   float scale;         // 1 / sqrt(d)
   float scale_log2;    // log2(e) / sqrt(d)
 };
@@ -59,14 +63,24 @@ struct Row {
 
 __device__ __forceinline__ bool decode_item(const AttnArgs &a, Row &r) {
   const int x = blockIdx.x;
-  const int L = (x % kXcds) * a.per_xcd + x / kXcds;
-  if (L >= a.n_items) return false;
   const int G = a.Hq / a.Hkv;
-  const int per_g = G * a.nbT;
-  r.g = L / per_g;
-  const int rem = L % per_g;
-  r.b = a.pd.order[rem / G];
-  r.h = r.g * G + rem % G;
+  if (a.split > 1) {
+    // XCD k: KV head k / split, ranks congruent to k % split, in order
+    const int k = x % kXcds, j = x / kXcds;
+    const int rank = k % a.split + a.split * (j / G);
+    if (rank >= a.nbT) return false;
+    r.g = k / a.split;
+    r.b = a.pd.order[rank];
+    r.h = r.g * G + j % G;
+  } else {
+    const int L = (x % kXcds) * a.per_xcd + x / kXcds;
+    if (L >= a.n_items) return false;
+    const int per_g = G * a.nbT;
+    r.g = L / per_g;
+    const int rem = L % per_g;
+    r.b = a.pd.order[rem / G];
+    r.h = r.g * G + rem % G;
+  }
   const int s = a.pd.blk_seq[r.b];
   r.i = r.b - a.pd.cu_blocks[s];
   r.seq_start = a.pd.cu_seqlens[s];
@@ -720,7 +734,14 @@ hipError_t launch_attn(const stem_plan_info &in, PlanDev pd, const void *q,
   a.kmax = in.kmax;
   a.T = in.total_tokens;
   a.n_items = static_cast<int32_t>(items);
-  a.per_xcd = static_cast<int32_t>((items + kXcds - 1) / kXcds);
+  if (in.num_kv_heads < kXcds && kXcds % in.num_kv_heads == 0) {
+    a.split = kXcds / in.num_kv_heads;
+    a.per_xcd = static_cast<int32_t>((in.num_q_heads / in.num_kv_heads) *
+                                     ((in.total_blocks + a.split - 1) / a.split));
+  } else {
+    a.split = 1;
+    a.per_xcd = static_cast<int32_t>((items + kXcds - 1) / kXcds);
+  }
   a.scale = 1.0f / sqrtf(static_cast<float>(in.head_dim));
   a.scale_log2 = a.scale * 1.4426950408889634f;
   const dim3 grid(static_cast<unsigned>(int64_t(a.per_xcd) * kXcds));
