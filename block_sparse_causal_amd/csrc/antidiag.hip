@@ -42,10 +42,39 @@
 // Kernel 2 (antidiag_metric_kernel): one wavefront per metric row turns the
 // row's block logits into the metric in place (row softmax times V magnitude,
 // the additive form, or the softmax alone).
+#include <type_traits>
+
 #include "stem_device.h"
 
 namespace stem {
 namespace {
+
+// f(std::integral_constant<int, I>()) for I = FIRST .. LAST - 1
+template <int FIRST, int LAST, typename F>
+__device__ __forceinline__ void static_for(F &&f) {
+  if constexpr (FIRST < LAST) {
+    f(std::integral_constant<int, FIRST>{});
+    static_for<FIRST + 1, LAST>(f);
+  }
+}
+
+// Two DMAs (see dma16x4) in one asm block: M0 saved and restored once.
+__device__ __forceinline__ void dma16x2(const void *g0, uint32_t v0, uint32_t l0,
+                                        const void *g1, uint32_t v1, uint32_t l1) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %5\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %3\n\t"
+      "s_mov_b32 m0, %6\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %2, %4\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(v0), "v"(v1), "s"(g0), "s"(g1), "s"(l0), "s"(l1)
+      : "memory");
+}
 
 constexpr int kTM = 256;                 // query groups per tile
 constexpr int kTN = 128;                 // key groups per tile
@@ -222,9 +251,33 @@ __global__ __launch_bounds__(256, 2) void antidiag_kernel(AdArgs a) {
   const char *ktile = a.k + (int64_t(t0) + int64_t(c0) * S) * krow + int64_t(hk) * D * 2;
   const int qlim = len - 1 - r0 * S, klim = len - 1 - c0 * S;   // last token, tile-relative
   const uint32_t lds0 = lds_addr_of(lds);
+  // whole tiles (every token of the tile's groups exists): the clamps never
+  // bind, each lane's byte offsets are constants and the token position u
+  // moves the scalar bases only
+  static_assert(kDmaA == 4 && kDmaB == 2, "DMA batches");
+  const bool qfull = (r0 + kTM) * S <= len, kfull = (c0 + kTN) * S <= len;
+  uint32_t qoff[kDmaA], koff[kDmaB];
+#pragma unroll
+  for (int x = 0; x < kDmaA; ++x) {
+    const int row = 16 * (w + 4 * x) + drow;
+    qoff[x] = uint32_t(row * S + S - 1) * uint32_t(qrow) + (((lane & 3) ^ swz_a(row)) * 16);
+  }
+#pragma unroll
+  for (int x = 0; x < kDmaB; ++x) {
+    const int row = 16 * (w + 4 * x) + drow;
+    koff[x] = uint32_t(row * S) * uint32_t(krow) + (((lane & 3) ^ swz_b(row)) * 16);
+  }
   auto issue = [&](int st, int buf) {
     const int u = st / QTR, qt = st - u * QTR;
     const uint32_t sb = lds0 + buf * kStage;
+    if (qfull && kfull) {
+      const char *ga = qtile + qt * 64 - int64_t(u) * qrow;
+      const char *gb = ktile + qt * 64 + int64_t(u) * krow;
+      dma16x4(ga, qoff[0], sb + (w + 0) * 1024, ga, qoff[1], sb + (w + 4) * 1024,
+              ga, qoff[2], sb + (w + 8) * 1024, ga, qoff[3], sb + (w + 12) * 1024);
+      dma16x2(gb, koff[0], sb + kAB + (w + 0) * 1024, gb, koff[1], sb + kAB + (w + 4) * 1024);
+      return;
+    }
 #pragma unroll
     for (int x = 0; x < kDmaA; ++x) {
       const int row = 16 * (w + 4 * x) + drow;
@@ -293,11 +346,11 @@ __global__ __launch_bounds__(256, 2) void antidiag_kernel(AdArgs a) {
 
   issue(0, 0);
   issue(1, 1);                             // nst >= 2 (S >= 1, D >= 64)
-  for (int st = 0; st < nst; ++st) {
+  auto stage = [&](int st, auto btag) {
+    constexpr int buf = decltype(btag)::value;
     if (st + 1 < nst) __builtin_amdgcn_s_waitcnt(0x0F70 | (kDmaA + kDmaB));
     else wait_vm();
     __syncthreads();
-    const int buf = st % kNBuf;
     if (partial) {
       const int u = st / QTR;
       char *A = lds + buf * kStage;
@@ -309,7 +362,7 @@ __global__ __launch_bounds__(256, 2) void antidiag_kernel(AdArgs a) {
       wait_lgkm();
       __syncthreads();
     }
-    if (st + 2 < nst) issue(st + 2, (st + 2) % kNBuf);
+    if (st + 2 < nst) issue(st + 2, (buf + 2) % kNBuf);
     if (!idle) compute(buf);
     if (diag_wave && st == st_freeze) {
 #pragma unroll
@@ -321,7 +374,12 @@ __global__ __launch_bounds__(256, 2) void antidiag_kernel(AdArgs a) {
             for (int e = 0; e < 16; ++e)
               if (e == e_diag) frozen[m] = acc[m][n][e];
     }
-  }
+  };
+  // unrolled over the buffers: every buffer offset is a constant
+  for (int st = 0; st < nst; st += kNBuf)
+    static_for<0, kNBuf>([&](auto b) {
+      if (st + decltype(b)::value < nst) stage(st + decltype(b)::value, b);
+    });
   if (diag_wave && has_diag) {
 #pragma unroll
     for (int m = 0; m < 2; ++m)
