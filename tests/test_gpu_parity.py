@@ -42,6 +42,15 @@ SMALL = {
                                sink_blocks=1, k_min=3, rho0=0.7, tau=5.0, seed=17),
     "f32-b128-d64": syn.custom([640], 2, 1, 64, "f32", 128,
                                sink_blocks=1, k_min=1, rho0=0.5, tau=2.0, seed=18),
+    # KV-head counts for each way the attention grid places work on the 8
+    # XCDs: 4 KV heads (each shared by two XCDs, 3 query heads per group),
+    # 3 (contiguous ranges) and 16 (two KV heads per XCD)
+    "bf16-b64-d128-hkv4-g3": syn.custom([900, 2000, 333], 12, 4, 128, "bf16", 64,
+                                        sink_blocks=2, k_min=3, rho0=0.5, tau=8.0, seed=19),
+    "bf16-b128-d64-hkv3-g2": syn.custom([1500, 700], 6, 3, 64, "bf16", 128,
+                                        sink_blocks=1, k_min=2, rho0=0.5, tau=4.0, seed=20),
+    "bf16-b64-d64-hkv16": syn.custom([700, 64], 16, 16, 64, "bf16", 64,
+                                     sink_blocks=1, k_min=2, rho0=0.6, tau=4.0, seed=21),
 }
 
 
