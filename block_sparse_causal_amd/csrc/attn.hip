@@ -3,7 +3,12 @@
 // gist.science/es "Implementacion" step 3, gist.science/fr 2.C step 3).
 //
 // Work unit: one (query head h, query block i) row = B query tokens, one
-// workgroup of B/32 wavefronts, each wavefront owning 32 query tokens.  The
+// workgroup of B/32 wavefronts, each wavefront owning 32 query tokens.  At
+// B = 64 (bf16 inputs, an even number of query heads per KV head, lists of
+// at most 32 blocks) a work unit is a pair of query heads of one KV head:
+// four wavefronts, two per head, stream the union of the two heads' lists
+// through one set of stage buffers, which lets three workgroups (three
+// wavefronts per SIMD) share a CU as at B = 128.  The
 // workgroup walks the row's kept key blocks in ascending order; each key
 // block (B tokens of K and V) is staged in LDS once and consumed by all
 // wavefronts.  Per wavefront and key block:
@@ -50,6 +55,7 @@ struct AttnArgs {
   int32_t n_items;     // Hq * nbT
   int32_t per_xcd;     // work items per XCD
   int32_t split;       // XCDs sharing one KV head (1: contiguous ranges)
+  int32_t hpi;         // query heads per work item (1, or 2 for head pairs)
   float scale;         // 1 / sqrt(d)
   float scale_log2;    // log2(e) / sqrt(d)
 };
@@ -59,28 +65,34 @@ struct Row {
   int64_t seq_start;
   int seq_len;
   const int32_t *list;
+  int h2, nkeep2;          // head pairs: the second head (-1: none) and its list
+  const int32_t *list2;
 };
 
 __device__ __forceinline__ bool decode_item(const AttnArgs &a, Row &r) {
   const int x = blockIdx.x;
   const int G = a.Hq / a.Hkv;
+  const int PG = (G + a.hpi - 1) / a.hpi;   // work items per (KV head, row)
+  int p;
   if (a.split > 1) {
     // XCD k: KV head k / split, ranks congruent to k % split, in order
     const int k = x % kXcds, j = x / kXcds;
-    const int rank = k % a.split + a.split * (j / G);
+    const int rank = k % a.split + a.split * (j / PG);
     if (rank >= a.nbT) return false;
     r.g = k / a.split;
     r.b = a.pd.order[rank];
-    r.h = r.g * G + j % G;
+    p = j % PG;
   } else {
     const int L = (x % kXcds) * a.per_xcd + x / kXcds;
     if (L >= a.n_items) return false;
-    const int per_g = G * a.nbT;
+    const int per_g = PG * a.nbT;
     r.g = L / per_g;
     const int rem = L % per_g;
-    r.b = a.pd.order[rem / G];
-    r.h = r.g * G + rem % G;
+    r.b = a.pd.order[rem / PG];
+    p = rem % PG;
   }
+  r.h = r.g * G + a.hpi * p;
+  r.h2 = (a.hpi == 2 && a.hpi * p + 1 < G) ? r.h + 1 : -1;
   const int s = a.pd.blk_seq[r.b];
   r.i = r.b - a.pd.cu_blocks[s];
   r.seq_start = a.pd.cu_seqlens[s];
@@ -88,6 +100,13 @@ __device__ __forceinline__ bool decode_item(const AttnArgs &a, Row &r) {
   const int64_t rowid = int64_t(r.h) * a.nbT + r.b;
   r.nkeep = min(a.count[rowid], a.kmax);
   r.list = a.idx + rowid * a.kmax;
+  r.nkeep2 = 0;
+  r.list2 = r.list;
+  if (r.h2 >= 0) {
+    const int64_t rowid2 = int64_t(r.h2) * a.nbT + r.b;
+    r.nkeep2 = min(a.count[rowid2], a.kmax);
+    r.list2 = a.idx + rowid2 * a.kmax;
+  }
   return true;
 }
 
@@ -153,15 +172,19 @@ __device__ __forceinline__ void static_for(F &&f) {
   }
 }
 
-template <int B, int D, int QW, bool OUT_BF16>
-__global__ __launch_bounds__(B / QW * 64)
-__attribute__((amdgpu_waves_per_eu(QW == 32 ? (B == 128 ? 3 : 2) : 1, QW == 32 ? (B == 128 ? 3 : 2) : 1)))
+template <int B, int D, int QW, bool OUT_BF16, bool PAIR>
+__global__ __launch_bounds__((PAIR ? 2 : 1) * B / QW * 64)
+__attribute__((amdgpu_waves_per_eu(QW == 32 ? (B == 128 || PAIR ? 3 : 2) : 1, QW == 32 ? (B == 128 || PAIR ? 3 : 2) : 1)))
 void attn_bf16_kernel(AttnArgs a) {
   constexpr int QT = QW / 32;          // 32-query tiles per wavefront
-  constexpr int NW = B / QW;           // wavefronts
+  // head pairs: two query heads of one KV head share a workgroup, wavefronts
+  // 0 .. B/QW - 1 on the first head and the rest on the second; the K/V
+  // stages stream the union of the two heads' lists, and a wavefront skips
+  // the blocks its head does not keep
+  constexpr int NW = (PAIR ? 2 : 1) * B / QW;   // wavefronts
   constexpr int NT = NW * 64;          // threads
   constexpr int SK = kStageKeys;       // keys per stage
-  constexpr int NBUF = stage_bufs<B>(); // stage buffers
+  constexpr int NBUF = PAIR ? 3 : stage_bufs<B>(); // stage buffers
   constexpr int NPB = B / SK;          // stages per key block
   constexpr int KT = SK / 32;          // 32-key MFMA tiles per stage
   constexpr int DT = D / 32;           // 32-dim output tiles
@@ -184,6 +207,10 @@ void attn_bf16_kernel(AttnArgs a) {
   const int hi = lane >> 5;
   const int Hq = a.Hq, Hkv = a.Hkv;
   const uint32_t lds_base = lds_addr_of(lds);
+  constexpr int WPH = B / QW;                    // wavefronts per head
+  const int wq = PAIR ? w % WPH : w;             // query slot of this wavefront
+  const int wh = PAIR ? w / WPH : 0;             // which head of the item
+  const int myh = wh == 0 ? r.h : r.h2;          // -1: no second head
 
   // Q fragments of this wavefront's QW queries (B operand of S^T = K Q^T):
   // tile qt holds queries w*QW + 32qt + n
@@ -191,10 +218,10 @@ void attn_bf16_kernel(AttnArgs a) {
   bf16x8 qf[QT][DC];
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt) {
-    qloc[qt] = r.i * B + w * QW + qt * 32 + n;
-    const bool qvalid = qloc[qt] < r.seq_len;
+    qloc[qt] = r.i * B + wq * QW + qt * 32 + n;
+    const bool qvalid = qloc[qt] < r.seq_len && myh >= 0;
     const uint16_t *qp = static_cast<const uint16_t *>(a.q) +
-                         ((r.seq_start + (qvalid ? qloc[qt] : 0)) * Hq + r.h) * int64_t(D) + hi * 8;
+                         ((r.seq_start + (qvalid ? qloc[qt] : 0)) * Hq + max(myh, 0)) * int64_t(D) + hi * 8;
 #pragma unroll
     for (int c = 0; c < DC; ++c) {
       u32x4 x = qvalid ? *reinterpret_cast<const u32x4 *>(qp + c * 16) : u32x4{0u, 0u, 0u, 0u};
@@ -303,7 +330,7 @@ void attn_bf16_kernel(AttnArgs a) {
     if constexpr (MASK) {
       // nothing visible to this wavefront in this stage (future keys or
       // past the end of the sequence): skip it (wave-uniform)
-      if (key0 > r.i * B + w * QW + QW - 1 || key0 >= r.seq_len) { after_s(); return; }
+      if (key0 > r.i * B + wq * QW + QW - 1 || key0 >= r.seq_len) { after_s(); return; }
     }
     const char *Kb = lds + buf * TILEB;
     const char *Vb = lds + (NBUF + buf) * TILEB;
@@ -332,7 +359,7 @@ void attn_bf16_kernel(AttnArgs a) {
         // key position <= query position, and inside the sequence
 #pragma unroll
         for (int qt = 0; qt < QT; ++qt) {
-          const int lim = min(r.i * B + w * QW + qt * 32 + n, r.seq_len - 1) - (key0 + u * 32 + 4 * hi);
+          const int lim = min(r.i * B + wq * QW + qt * 32 + n, r.seq_len - 1) - (key0 + u * 32 + 4 * hi);
 #pragma unroll
           for (int q = 0; q < 16; ++q)
             if (8 * (q >> 2) + (q & 3) > lim) sacc[u][qt][q] = -INFINITY;
@@ -426,16 +453,58 @@ void attn_bf16_kernel(AttnArgs a) {
   // Kept block numbers, 64 at a time in one register (lane e holds entry
   // chunk + e); entries outside [0, i] are clamped so that no access leaves
   // the sequence.
-  const int nkeep = r.nkeep;
+  // head pairs: the union of the two ascending lists (at most 32 entries
+  // each), every entry tagged with the heads that keep it (bit 28: first,
+  // bit 29: second), built by each wavefront in its own LDS slot of the last
+  // stage buffer (whose first DMA goes out after the first stage's barrier)
+  constexpr uint32_t kBlockMask = (1u << 28) - 1;
+  int nkeep = r.nkeep;
   int chunk = 0;
   int listv = lane < nkeep ? min(max(r.list[lane], 0), r.i) : 0;
-  auto entry = [&](int t) {
-    if (t >= chunk + 64) {
-      chunk += 64;
-      listv = chunk + lane < nkeep ? min(max(r.list[chunk + lane], 0), r.i) : 0;
+  if constexpr (PAIR) {
+    const int n0 = r.nkeep, n1 = r.nkeep2;
+    const int x0 = lane < n0 ? min(max(r.list[lane], 0), r.i) : 0;
+    const int x1 = lane < n1 ? min(max(r.list2[lane], 0), r.i) : 0;
+    // second-list entries: also in the first list? how many first-list
+    // entries are smaller?
+    bool dup1 = false;
+    int lt0 = 0;
+    for (int j = 0; j < n0; ++j) {
+      const int y = __builtin_amdgcn_readlane(x0, j);
+      dup1 |= y == x1;
+      lt0 += y < x1;
     }
-    return __builtin_amdgcn_readlane(listv, t - chunk);
+    const uint64_t dupm = __ballot(lane < n1 && dup1);
+    // first-list entries: how many second-list-only entries are smaller,
+    // and is it kept by the second head too?
+    bool in1 = false;
+    int lt1 = 0;
+    for (int j = 0; j < n1; ++j) {
+      const int y = __builtin_amdgcn_readlane(x1, j);
+      in1 |= y == x0;
+      lt1 += (y < x0) && !((dupm >> j) & 1);
+    }
+    int32_t *slot = reinterpret_cast<int32_t *>(lds + (NBUF - 1) * TILEB) + w * 64;
+    if (lane < n0) slot[lane + lt1] = x0 | (1 << 28) | (in1 ? (1 << 29) : 0);
+    const int dups_below = __popcll(dupm & ((uint64_t(1) << lane) - 1));
+    if (lane < n1 && !dup1) slot[lt0 + lane - dups_below] = x1 | (1 << 29);
+    nkeep = n0 + n1 - __popcll(dupm);
+    wait_lgkm();
+    listv = lane < nkeep ? slot[lane] : 0;
+  }
+  // entry t of the stream (packed with the head tags for head pairs)
+  auto entry = [&](int t) {
+    if constexpr (PAIR) {
+      return __builtin_amdgcn_readlane(listv, t);
+    } else {
+      if (t >= chunk + 64) {
+        chunk += 64;
+        listv = chunk + lane < nkeep ? min(max(r.list[chunk + lane], 0), r.i) : 0;
+      }
+      return __builtin_amdgcn_readlane(listv, t - chunk);
+    }
   };
+  const int mybit = 28 + wh;
 
   // Stage s covers keys [p*SK, p*SK + SK) of entry s / NPB (p = s % NPB) and
   // lives in buffer s % NBUF; its DMA is issued NBUF - 1 stages ahead.
@@ -446,7 +515,7 @@ void attn_bf16_kernel(AttnArgs a) {
     for (int e = 0; e < NBUF; ++e) jq[e] = 0;
 #pragma unroll
     for (int e = 0; e < NBUF - 1; ++e)
-      if (e < nst) { jq[e] = entry(e / NPB); issue(jq[e], e % NPB, e); }
+      if (e < nst) { jq[e] = entry(e / NPB); issue(jq[e] & kBlockMask, e % NPB, e); }
     auto body = [&](int st, auto btag, auto mtag) {
       constexpr int buf = decltype(btag)::value;
       // this stage's DMA has landed once at most the later stages' loads
@@ -454,15 +523,24 @@ void attn_bf16_kernel(AttnArgs a) {
       if (NBUF > 2 && st + NBUF - 2 < nst) __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * LOADS * (NBUF - 2)));
       else wait_vm();
       __syncthreads();
-      const int key0 = jq[0] * B + (st % NPB) * SK;
+      const int key0 = int(jq[0] & kBlockMask) * B + (st % NPB) * SK;
       const int nxt = st + NBUF - 1;
       auto after = [&] {
         if (nxt < nst) {
           jq[NBUF - 1] = entry(nxt / NPB);
-          issue(jq[NBUF - 1], nxt % NPB, (buf + NBUF - 1) % NBUF);
+          issue(jq[NBUF - 1] & kBlockMask, nxt % NPB, (buf + NBUF - 1) % NBUF);
         }
       };
-      step(mtag, buf, key0, after);
+      // head pairs: a block the wavefront's head does not keep only moves
+      // the ring on
+      if constexpr (PAIR) {
+        // head pairs: the next stage's DMA first, then this stage's products
+        // only if this wavefront's head keeps the block
+        after();
+        if ((jq[0] >> mybit) & 1) step(mtag, buf, key0, [] {});
+      } else {
+        step(mtag, buf, key0, after);
+      }
 #pragma unroll
       for (int e = 0; e + 1 < NBUF; ++e) jq[e] = jq[e + 1];
     };
@@ -490,6 +568,7 @@ void attn_bf16_kernel(AttnArgs a) {
     const int lane = opaque_lane_id();
     const int n = lane & 31, hi = lane >> 5;
     char *ot = lds + w * (32 * D * 2);
+    if (myh < 0) return;
     const float ltot = lrun[0] + __shfl_xor(lrun[0], 32);
     const float inv = 1.0f / ltot;
 #pragma unroll
@@ -508,24 +587,25 @@ void attn_bf16_kernel(AttnArgs a) {
       const int row = it * ROWS_PER_STORE + lane / NCH;
       const int c = lane % NCH;
       const u32x4 v = *reinterpret_cast<const u32x4 *>(ot + row * (D * 2) + ((c ^ (row % NCH)) * 16));
-      const int qpos = r.i * B + w * QW + row;
+      const int qpos = r.i * B + wq * QW + row;
       if (qpos < r.seq_len)
         // non-temporal: O is not read again here, and keeping it out of L2
         // leaves room for the K/V blocks that neighbouring rows reuse
         __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(static_cast<uint16_t *>(a.out) +
-                                   ((r.seq_start + qpos) * Hq + r.h) * int64_t(D) + c * 8));
+                                   ((r.seq_start + qpos) * Hq + myh) * int64_t(D) + c * 8));
     }
-    const int q0 = r.i * B + w * QW + n;
+    const int q0 = r.i * B + wq * QW + n;
     if (a.lse && hi == 0 && q0 < r.seq_len)
-      a.lse[int64_t(r.h) * a.T + r.seq_start + q0] = mrun[0] * a.scale + logf(ltot);
+      a.lse[int64_t(myh) * a.T + r.seq_start + q0] = mrun[0] * a.scale + logf(ltot);
     return;
   }
+  if (myh < 0) return;
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt) {
     const float ltot = lrun[qt] + __shfl_xor(lrun[qt], 32);
     if (qloc[qt] >= r.seq_len) continue;
     const float inv = 1.0f / ltot;
-    const int64_t orow = ((r.seq_start + qloc[qt]) * Hq + r.h) * int64_t(D);
+    const int64_t orow = ((r.seq_start + qloc[qt]) * Hq + myh) * int64_t(D);
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
@@ -542,7 +622,7 @@ void attn_bf16_kernel(AttnArgs a) {
         }
       }
     if (a.lse && hi == 0)
-      a.lse[int64_t(r.h) * a.T + r.seq_start + qloc[qt]] = mrun[qt] * a.scale + logf(ltot);
+      a.lse[int64_t(myh) * a.T + r.seq_start + qloc[qt]] = mrun[qt] * a.scale + logf(ltot);
   }
 }
 
@@ -695,8 +775,14 @@ constexpr int kQW = 32;
 
 template <bool BF16IN, int B, int D, bool OB>
 hipError_t launch_one(const AttnArgs &a, dim3 grid, hipStream_t st) {
+  if constexpr (B == 64 && BF16IN) {
+    if (a.hpi == 2) {
+      hipLaunchKernelGGL((attn_bf16_kernel<B, D, kQW, OB, true>), grid, dim3(2 * B / kQW * 64), 0, st, a);
+      return hipGetLastError();
+    }
+  }
   if (BF16IN)
-    hipLaunchKernelGGL((attn_bf16_kernel<B, D, kQW, OB>), grid, dim3(B / kQW * 64), 0, st, a);
+    hipLaunchKernelGGL((attn_bf16_kernel<B, D, kQW, OB, false>), grid, dim3(B / kQW * 64), 0, st, a);
   else
     hipLaunchKernelGGL((attn_f32_kernel<B, D, OB>), grid, dim3(B * 2), 0, st, a);
   return hipGetLastError();
@@ -734,13 +820,20 @@ hipError_t launch_attn(const stem_plan_info &in, PlanDev pd, const void *q,
   a.kmax = in.kmax;
   a.T = in.total_tokens;
   a.n_items = static_cast<int32_t>(items);
+  // head pairs for bf16 inputs at B = 64 with an even number of query heads
+  // per KV head (an odd one would leave half of a workgroup idle) and lists
+  // of at most 32 entries (their union fits one register)
+  a.hpi = (in.dtype == STEM_BF16 && in.block == 64 && in.kmax <= 32 &&
+           (in.num_q_heads / in.num_kv_heads) % 2 == 0) ? 2 : 1;
+  const int PG = (in.num_q_heads / in.num_kv_heads + a.hpi - 1) / a.hpi;
+  const int64_t units = int64_t(in.num_kv_heads) * PG * in.total_blocks;
+  a.n_items = static_cast<int32_t>(units);
   if (in.num_kv_heads < kXcds && kXcds % in.num_kv_heads == 0) {
     a.split = kXcds / in.num_kv_heads;
-    a.per_xcd = static_cast<int32_t>((in.num_q_heads / in.num_kv_heads) *
-                                     ((in.total_blocks + a.split - 1) / a.split));
+    a.per_xcd = static_cast<int32_t>(PG * ((in.total_blocks + a.split - 1) / a.split));
   } else {
     a.split = 1;
-    a.per_xcd = static_cast<int32_t>((items + kXcds - 1) / kXcds);
+    a.per_xcd = static_cast<int32_t>((units + kXcds - 1) / kXcds);
   }
   a.scale = 1.0f / sqrtf(static_cast<float>(in.head_dim));
   a.scale_log2 = a.scale * 1.4426950408889634f;

@@ -51,6 +51,9 @@ SMALL = {
                                         sink_blocks=1, k_min=2, rho0=0.5, tau=4.0, seed=20),
     "bf16-b64-d64-hkv16": syn.custom([700, 64], 16, 16, 64, "bf16", 64,
                                      sink_blocks=1, k_min=2, rho0=0.6, tau=4.0, seed=21),
+    # B = 64, d = 64 with two query heads per KV head: the head-pair kernel
+    "bf16-b64-d64-pairs": syn.custom([1500, 333, 64], 4, 2, 64, "bf16", 64,
+                                     sink_blocks=2, k_min=3, rho0=0.5, tau=6.0, seed=22),
 }
 
 
