@@ -4,8 +4,9 @@
 //
 // Work unit: one (query head h, query block i) row = B query tokens, one
 // workgroup of B/32 wavefronts, each wavefront owning 32 query tokens.  At
-// B = 64 (bf16 inputs, an even number of query heads per KV head, lists of
-// at most 32 blocks) a work unit is a pair of query heads of one KV head:
+// B = 64 (bf16 inputs, lists of at most 32 blocks) a work unit is a pair of
+// query heads of one KV head (with an odd number of query heads per KV head
+// the last one runs as single-head units in a second launch):
 // four wavefronts, two per head, stream the union of the two heads' lists
 // through one set of stage buffers, which lets three workgroups (three
 // wavefronts per SIMD) share a CU as at B = 128.  The
@@ -56,6 +57,7 @@ struct AttnArgs {
   int32_t per_xcd;     // work items per XCD
   int32_t split;       // XCDs sharing one KV head (1: contiguous ranges)
   int32_t hpi;         // query heads per work item (1, or 2 for head pairs)
+  int32_t hoff, hgrp;  // query heads hoff .. hoff + hgrp - 1 of each KV head's group
   float scale;         // 1 / sqrt(d)
   float scale_log2;    // log2(e) / sqrt(d)
 };
@@ -72,7 +74,7 @@ struct Row {
 __device__ __forceinline__ bool decode_item(const AttnArgs &a, Row &r) {
   const int x = blockIdx.x;
   const int G = a.Hq / a.Hkv;
-  const int PG = (G + a.hpi - 1) / a.hpi;   // work items per (KV head, row)
+  const int PG = a.hgrp / a.hpi;            // work items per (KV head, row)
   int p;
   if (a.split > 1) {
     // XCD k: KV head k / split, ranks congruent to k % split, in order
@@ -91,8 +93,8 @@ __device__ __forceinline__ bool decode_item(const AttnArgs &a, Row &r) {
     r.b = a.pd.order[rem / PG];
     p = rem % PG;
   }
-  r.h = r.g * G + a.hpi * p;
-  r.h2 = (a.hpi == 2 && a.hpi * p + 1 < G) ? r.h + 1 : -1;
+  r.h = r.g * G + a.hoff + a.hpi * p;
+  r.h2 = a.hpi == 2 ? r.h + 1 : -1;
   const int s = a.pd.blk_seq[r.b];
   r.i = r.b - a.pd.cu_blocks[s];
   r.seq_start = a.pd.cu_seqlens[s];
@@ -819,28 +821,42 @@ hipError_t launch_attn(const stem_plan_info &in, PlanDev pd, const void *q,
   a.nbT = static_cast<int32_t>(in.total_blocks);
   a.kmax = in.kmax;
   a.T = in.total_tokens;
-  a.n_items = static_cast<int32_t>(items);
-  // head pairs for bf16 inputs at B = 64 with an even number of query heads
-  // per KV head (an odd one would leave half of a workgroup idle) and lists
-  // of at most 32 entries (their union fits one register)
-  a.hpi = (in.dtype == STEM_BF16 && in.block == 64 && in.kmax <= 32 &&
-           (in.num_q_heads / in.num_kv_heads) % 2 == 0) ? 2 : 1;
-  const int PG = (in.num_q_heads / in.num_kv_heads + a.hpi - 1) / a.hpi;
-  const int64_t units = int64_t(in.num_kv_heads) * PG * in.total_blocks;
-  a.n_items = static_cast<int32_t>(units);
-  if (in.num_kv_heads < kXcds && kXcds % in.num_kv_heads == 0) {
-    a.split = kXcds / in.num_kv_heads;
-    a.per_xcd = static_cast<int32_t>(PG * ((in.total_blocks + a.split - 1) / a.split));
-  } else {
-    a.split = 1;
-    a.per_xcd = static_cast<int32_t>((units + kXcds - 1) / kXcds);
-  }
+  // Head pairs for bf16 inputs at B = 64 with lists of at most 32 entries
+  // (their union fits one register).  With an odd number of query heads per
+  // KV head, the last head of every group takes a second launch of
+  // single-head work items.
+  const int G = in.num_q_heads / in.num_kv_heads;
+  const bool pairs = in.dtype == STEM_BF16 && in.block == 64 && in.kmax <= 32 && G >= 2;
+  auto setup = [&](int hpi, int hoff, int hgrp) {
+    a.hpi = hpi; a.hoff = hoff; a.hgrp = hgrp;
+    const int PG = hgrp / hpi;
+    const int64_t units = int64_t(in.num_kv_heads) * PG * in.total_blocks;
+    a.n_items = static_cast<int32_t>(units);
+    if (in.num_kv_heads < kXcds && kXcds % in.num_kv_heads == 0) {
+      a.split = kXcds / in.num_kv_heads;
+      a.per_xcd = static_cast<int32_t>(PG * ((in.total_blocks + a.split - 1) / a.split));
+    } else {
+      a.split = 1;
+      a.per_xcd = static_cast<int32_t>((units + kXcds - 1) / kXcds);
+    }
+  };
   a.scale = 1.0f / sqrtf(static_cast<float>(in.head_dim));
   a.scale_log2 = a.scale * 1.4426950408889634f;
-  const dim3 grid(static_cast<unsigned>(int64_t(a.per_xcd) * kXcds));
   const bool ob = out_dtype == STEM_BF16;
-  if (in.dtype == STEM_BF16) return launch_dtype<true>(a, grid, in.block, in.head_dim, ob, st);
-  return launch_dtype<false>(a, grid, in.block, in.head_dim, ob, st);
+  auto launch = [&]() {
+    const dim3 grid(static_cast<unsigned>(int64_t(a.per_xcd) * kXcds));
+    if (in.dtype == STEM_BF16) return launch_dtype<true>(a, grid, in.block, in.head_dim, ob, st);
+    return launch_dtype<false>(a, grid, in.block, in.head_dim, ob, st);
+  };
+  if (!pairs) {
+    setup(1, 0, G);
+    return launch();
+  }
+  setup(2, 0, G - G % 2);
+  hipError_t e = launch();
+  if (e != hipSuccess || G % 2 == 0) return e;
+  setup(1, G - 1, 1);
+  return launch();
 }
 
 }  // namespace stem
