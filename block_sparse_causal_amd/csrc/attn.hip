@@ -123,10 +123,12 @@ __device__ __forceinline__ bool decode_item(const AttnArgs &a, Row &r) {
 // ahead, and with at most 168 VGPRs per wavefront three workgroups share a
 // CU (three wavefronts per SIMD): their barriers are independent, so one's
 // softmax, LDS reads and DMA waits overlap the others' MFMAs.  At B = 64
-// (two-wavefront workgroups) the kernel needs more than 170 VGPRs, so two
+// single-head (two-wavefront) workgroups need more than 170 VGPRs, so two
 // wavefronts per SIMD (four workgroups per CU) is the register bound; two
 // stage buffers (32 KiB at d = 128) fit four workgroups, three would leave
-// LDS for only three.
+// LDS for only three.  B = 64 head-pair workgroups (PAIR) have the B = 128
+// shape (four wavefronts, two loads per thread and operand, three stage
+// buffers) and the same 168-VGPR bound, so three of them share a CU.
 //
 // K and V stages are row-major with an XOR swizzle of the 16-byte chunks:
 // K operand reads (ds_read_b128 of one key row) and V operand reads
