@@ -54,6 +54,12 @@ SMALL = {
     # B = 64, d = 64 with two query heads per KV head: the head-pair kernel
     "bf16-b64-d64-pairs": syn.custom([1500, 333, 64], 4, 2, 64, "bf16", 64,
                                      sink_blocks=2, k_min=3, rho0=0.5, tau=6.0, seed=22),
+    # uniform budgets of 2 sinks + 1 diagonal + k_min: lists of 32 blocks (the
+    # longest the head-pair kernel takes) and of 33 (single-head workgroups)
+    "bf16-b64-d128-lists32": syn.custom([64 * 45, 500], 4, 2, 128, "bf16", 64,
+                                        sink_blocks=2, k_min=29, rho0=0.0, tau=1.0, seed=23),
+    "bf16-b64-d128-lists33": syn.custom([64 * 45, 500], 4, 2, 128, "bf16", 64,
+                                        sink_blocks=2, k_min=30, rho0=0.0, tau=1.0, seed=24),
 }
 
 
