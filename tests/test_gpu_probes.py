@@ -9,6 +9,13 @@ from block_sparse_causal_amd import stem
 pytestmark = pytest.mark.gpu
 
 
+@pytest.fixture(autouse=True)
+def _cuda():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
 def test_mfma_probe_reports_work_and_finite_results():
     import torch
     sink = torch.full((4096,), float("nan"), dtype=torch.float32, device="cuda")
