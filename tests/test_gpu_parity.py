@@ -324,3 +324,29 @@ def test_maximum_sequence_length():
     w = syn.custom([64 * 4096], 2, 1, 64, "bf16", 64, sink_blocks=2, k_min=8, rho0=0.5,
                    tau=64.0, seed=61).replace(name="max-seq-4096-blocks")
     _full_size(w, 48)
+
+
+def _random_case(seed: int):
+    """A seeded random small bf16 workload: head shape, block size, sequence
+    lengths (with partial and very short sequences), budget and metric."""
+    rng = np.random.default_rng(1000 + seed)
+    hkv = int(rng.choice([1, 2, 3, 4]))
+    g = int(rng.integers(1, 6))
+    B = int(rng.choice([64, 128]))
+    d = int(rng.choice([64, 128]))
+    nseq = int(rng.integers(1, 4))
+    lens = [int(x) for x in rng.integers(1, 40 * B, size=nseq)]
+    metric = str(rng.choice(["output_aware", "additive", "routing"]))
+    kw = dict(sink_blocks=int(rng.integers(0, 4)), k_min=int(rng.integers(1, 40)),
+              rho0=float(rng.uniform(0.0, 1.0)), tau=float(rng.uniform(1.0, 16.0)),
+              seed=200 + seed, metric=metric)
+    return syn.custom(lens, g * hkv, hkv, d, "bf16", B, **kw)
+
+
+@pytest.mark.parametrize("seed", range(20))
+def test_random_small_workloads_every_stage(seed):
+    _cuda()
+    w = _random_case(seed)
+    H.log(f"case random {seed}: lens {w.seqlens} heads {w.num_q_heads}/{w.num_kv_heads} "
+          f"d {w.head_dim} B {w.block} metric {w.metric}")
+    _full_check(H.DeviceRun(w))
