@@ -20,7 +20,9 @@ Reported (one JSON line on stdout, progress on stderr):
   ceilings    the chip's matrix-core rate on random and on constant bf16
               operands and its streaming HBM read rate, re-measured by the
               library's probe kernels (the published peaks assume neither
-              the power limit nor the memory system's efficiency)
+              the power limit nor the memory system's efficiency), and the
+              attention kernel's time on its own block lists with V, Q, or
+              Q, K and V set to zero (same work, operands that do not toggle)
   cpu_baseline  the CPU oracle timed stage by stage on a bounded sample and
               scaled up (fp64, the oracle's precision, plus an fp32 line)
   step_ms_spread / attn_ms_spread  mean, median, min and max of the timed
@@ -248,6 +250,32 @@ def measure_ceilings(reps: int = 5):
     return out
 
 
+def operand_sensitivity(plan, q, k, v, bufs, reps: int = 5):
+    """The attention kernel on the step's own block lists, with the real
+    operands and with V, with Q, and with Q, K and V replaced by zeros: the
+    same instructions, LDS and memory traffic on operands whose bits do not
+    toggle.  Median ms of reps alternating rounds (one launch per operand set
+    and round)."""
+    import torch
+    from block_sparse_causal_amd import stem
+    st = torch.cuda.current_stream()
+    zq, zk, zv = torch.zeros_like(q), torch.zeros_like(k), torch.zeros_like(v)
+    sets = {"real": (q, k, v), "zero_v": (q, k, zv), "zero_q": (zq, k, v), "zero_qkv": (zq, zk, zv)}
+    out, lse = torch.empty_like(bufs.out), torch.empty_like(bufs.lse)
+    ms = {n: [] for n in sets}
+    for _ in range(reps):
+        for n, (qq, kk, vv) in sets.items():
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(st)
+            stem.stem_sparse_attn(plan, qq, kk, vv, bufs.idx, bufs.count, out, lse, st)
+            b.record(st)
+            b.synchronize()
+            ms[n].append(a.elapsed_time(b))
+    del zq, zk, zv, out, lse
+    torch.cuda.empty_cache()
+    return {n: round(float(np.median(t)), 4) for n, t in ms.items()}
+
+
 def copy_calibration(nbytes: int = 1 << 30):
     """One device-to-device copy of a known size, for scaling the hardware
     byte counters of a profiling run (its kernel reads and writes nbytes)."""
@@ -441,6 +469,11 @@ def main():
                                           else arec["fetch_bytes"] + arec["write_bytes"]),
                               "flop_per_launch": af, "avg_launch_ms": round(stage_ms["score"], 4)}
         log(f"antidiag stride {args.score_stride}: {stage_ms['score']:.3f} ms, {ach:.1f} TFLOP/s")
+    operands = None
+    if not args.no_ceilings:
+        log("attention on zeroed operands (same block lists)")
+        operands = operand_sensitivity(plan, q, k, v, bufs)
+        log(f"attention ms by operands: {operands}")
     del bufs
 
     if not args.no_dense:
@@ -456,6 +489,7 @@ def main():
         c = measure_ceilings()
         c["attn_frac_of_random_mfma"] = round(achieved / c["mfma_bf16_random_tflops"], 4)
         c["pool_frac_of_hbm_read"] = round(result["hbm_gbs"]["pool"] / c["hbm_read_gbs"], 4)
+        c["attn_ms_by_operands"] = operands
         result["ceilings"] = c
         log(f"ceilings: {c}")
 

@@ -1,7 +1,8 @@
 """The bench.py output line on a GPU: one JSON object on stdout with the
 fields its readers depend on (the metric, the timing, the roofline of the
 attention kernel and the CPU oracle baseline), on a small layer so that it
-finishes in seconds."""
+finishes in seconds (with the probe kernels and the zero-operand attention
+timings)."""
 import json
 import os
 import subprocess
@@ -25,7 +26,7 @@ def test_bench_line_fields():
     print("case bench line llama3-8b-32k-b64", flush=True)
     r = subprocess.run([sys.executable, "-u", os.path.join(ROOT, "bench.py"),
                         "--workload", "llama3-8b-32k-b64", "--steps", "3", "--warmup", "1",
-                        "--no-dense", "--no-ceilings"],
+                        "--no-dense"],
                        capture_output=True, text=True, timeout=280, cwd=ROOT)
     assert r.returncode == 0, r.stderr[-2000:]
     lines = [l for l in r.stdout.splitlines() if l.strip()]
@@ -48,6 +49,10 @@ def test_bench_line_fields():
     assert 0 < j["stages_ms"]["attn"] < j["value"]
     s = j["step_ms_spread"]
     assert s["min"] <= s["median"] <= s["max"]
+    c = j["ceilings"]
+    assert c["mfma_bf16_random_tflops"] > 0 and c["hbm_read_gbs"] > 0
+    assert set(c["attn_ms_by_operands"]) == {"real", "zero_v", "zero_q", "zero_qkv"}
+    assert all(t > 0 for t in c["attn_ms_by_operands"].values())
     cb = j["cpu_baseline"]
     assert cb["kind"] == "oracle" and cb["unit"] == "ms" and cb["value"] > 0 and cb["cores"] >= 1
     assert set(cb["stages_ms"]) == {"pool", "score", "budget_select", "attn"}
