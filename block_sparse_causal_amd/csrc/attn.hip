@@ -494,7 +494,11 @@ void attn_bf16_kernel(AttnArgs a) {
     if (lane < n1 && !dup1) slot[lt0 + lane - dups_below] = x1 | (1 << 29);
     nkeep = n0 + n1 - __popcll(dupm);
     wait_lgkm();
-    listv = lane < nkeep ? slot[lane] : 0;
+    // with ascending lists every slot below nkeep is written once; lists out
+    // of order can leave slots unwritten, so the block part is clamped again
+    // (no access outside the sequence, whatever the slot holds)
+    const uint32_t e = uint32_t(slot[lane]);
+    listv = lane < nkeep ? int((e & ~kBlockMask) | min(e & kBlockMask, uint32_t(r.i))) : 0;
   }
   // entry t of the stream (packed with the head tags for head pairs)
   auto entry = [&](int t) {

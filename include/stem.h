@@ -225,9 +225,10 @@ int stem_select(const stem_plan_info *info, const void *plan_dev,
  *   o_t = sum_s softmax_s(q_t . k_s / sqrt(d)) v_s
  * out is [T, Hq, d] in out_dtype (STEM_F32 or STEM_BF16); lse, if not
  * NULL, is f32 [Hq, T] holding the natural-log sum of exp of the scaled
- * logits of each query token.  Listed blocks must lie in [0, i] (an entry
- * outside that range leads to no access outside the sequence, but its
- * result is not defined), and every row must list at least one block
+ * logits of each query token.  Listed blocks must lie in [0, i], in
+ * ascending order (an entry outside that range, or a list out of order,
+ * leads to no access outside the sequence, but the result is not defined),
+ * and every row must list at least one block
  * (stem_select always keeps the diagonal block; a row with count 0 has no
  * defined output). */
 int stem_sparse_attn(const stem_plan_info *info, const void *plan_dev,
