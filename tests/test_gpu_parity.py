@@ -235,6 +235,54 @@ def test_select_long_budget_and_wide_ties():
     H.select_rows_crossfed(r, H.all_rows(r))
 
 
+def _special_scores(n: int, rng: np.random.Generator) -> np.ndarray:
+    """Metric values with every class the selection orders specially: NaN
+    (ranks last), -0 and +0 (equal), +-inf, negatives, denormals and runs of
+    equal values, mixed with ordinary values."""
+    pool = np.array([np.nan, -np.inf, np.inf, -0.0, 0.0, -2.5, -1e-30, 1e-42, 0.25, 0.25, 3.0,
+                     1.0, 1.0, 7.5, 1e30], dtype=np.float32)
+    m = rng.standard_normal(n).astype(np.float32)
+    pick = rng.random(n) < 0.6
+    m[pick] = pool[rng.integers(0, pool.size, int(pick.sum()))]
+    return m
+
+
+@pytest.mark.parametrize("k_min,block", [(5, 64), (40, 64), (100, 64), (3, 128)])
+def test_select_special_metric_values(k_min, block):
+    """stem_select on metric rows holding NaN, signed zeros, infinities,
+    negatives and wide ties (written straight into the metric buffer): the
+    kept lists must equal the oracle's selection on the same values, every
+    row, both selection strategies (budgets up to and above 64 free slots)."""
+    _cuda()
+    import torch
+    cu = [0, block * 300, block * 300 + 17, block * 300 + 17 + block * 70 + 5]
+    Hq = 2
+    H.log(f"case select special values k_min={k_min} B={block}")
+    plan = stem.stem_plan(cu, Hq, 1, 128, block, "bf16", 2, k_min, 0.5, 8.0).to("cuda")
+    i = plan.info
+    rng = np.random.default_rng(1000 + k_min + block)
+    m = np.stack([_special_scores(int(i.score_elems_per_head), rng) for _ in range(Hq)])
+    scores = torch.from_numpy(m).to("cuda")
+    idx = torch.full((Hq, i.total_blocks, i.kmax), -7, dtype=torch.int32, device="cuda")
+    count = torch.full((Hq, i.total_blocks), -7, dtype=torch.int32, device="cuda")
+    stem.stem_select(plan, scores, idx, count)
+    torch.cuda.synchronize()
+    idx, count = idx.cpu().numpy(), count.cpu().numpy()
+    cub = O.block_layout(cu, block)
+    bud = O.budgets_for(cub, 2, k_min, 0.5, 8.0)
+    offs, _ = O.score_offsets(cub)
+    for h in range(Hq):
+        for s in range(len(cub) - 1):
+            for r in range(int(cub[s + 1] - cub[s])):
+                b = int(cub[s]) + r
+                row0 = int(offs[s]) + O.tri(r)
+                want = O.select_row(m[h, row0:row0 + r + 1].astype(np.float64), r, int(bud[b]), 2)
+                n = int(count[h, b])
+                assert n == want.size, (h, b, n, want.size)
+                assert np.array_equal(idx[h, b, :n], want), (h, b, idx[h, b, :n], want)
+                assert np.all(idx[h, b, n:] == -1), (h, b)
+
+
 # ----------------------------------------------------------------- full size
 
 
