@@ -283,6 +283,94 @@ def test_select_special_metric_values(k_min, block):
                 assert np.all(idx[h, b, n:] == -1), (h, b)
 
 
+def _moving_max_inputs(w, slope: float, gain: float, seed: int):
+    """Q and K sharing one direction (dimension 0) along which a key's logit
+    (after the 1/sqrt(d) scale) grows by ``slope`` per token position in its
+    sequence (falls, for a negative slope), over noise scaled by ``gain``:
+    the running maximum of a row moves at every stage (slope > 0), sits on
+    the first keys while later weights underflow (slope < 0), or jumps about
+    (slope 0, large gain).  V is scaled by 1/8 (exactly): with a few keys
+    carrying each row, the output is close to single rows of V, and the bf16
+    rounding of the weights (relative 2^-9) then costs a part of |v| that the
+    absolute bar should not see."""
+    x = syn.generate(w, seed=seed)
+    q, k = x.q * gain, x.k * gain
+    if w.dtype == "bf16":
+        x.v_bits = syn.bf16_bits(x.v * np.float32(0.125))
+        x.v = syn.bf16_bits_to_f32(x.v_bits)
+    else:
+        x.v = x.v * np.float32(0.125)
+    cu = w.cu_seqlens
+    beta = 4.0
+    alpha = slope * np.sqrt(w.head_dim) / beta
+    for si in range(len(cu) - 1):
+        t = np.arange(cu[si + 1] - cu[si], dtype=np.float32)
+        k[cu[si]:cu[si + 1], :, 0] = alpha * t[:, None]
+        q[cu[si]:cu[si + 1], :, 0] = beta
+    if w.dtype == "bf16":
+        x.q_bits, x.k_bits = syn.bf16_bits(q), syn.bf16_bits(k)
+        x.q, x.k = syn.bf16_bits_to_f32(x.q_bits), syn.bf16_bits_to_f32(x.k_bits)
+    else:
+        x.q, x.k = q, k
+    return x
+
+
+MOVING_MAX = {
+    # head pairs (lists of at most 32 blocks), single-head B = 64 (longer
+    # lists) and B = 128; bf16 inputs (with f32 inputs logits this large
+    # leave the 1e-5 bars below f32's own resolution)
+    "bf16-b64-pairs": syn.custom([64 * 20 + 13, 64 * 3], 4, 2, 128, "bf16", 64, sink_blocks=2,
+                                 k_min=6, rho0=0.5, tau=8.0, seed=61),
+    "bf16-b64-long": syn.custom([64 * 50 + 7], 2, 1, 128, "bf16", 64, sink_blocks=2,
+                                k_min=40, rho0=0.5, tau=8.0, seed=62),
+    "bf16-b128": syn.custom([128 * 12 + 77, 300], 4, 1, 128, "bf16", 128, sink_blocks=1,
+                            k_min=4, rho0=0.5, tau=8.0, seed=63),
+}
+
+
+@pytest.mark.parametrize("slope,gain", [(0.5, 1.0), (-0.5, 1.0), (0.0, 6.0)])
+@pytest.mark.parametrize("name", list(MOVING_MAX))
+def test_attention_moving_maximum(name, slope, gain):
+    """The attention kernel's online softmax where a row's maximum logit
+    moves at every stage (reference raised each time), stays on the first
+    keys (later weights underflow), or jumps by tens of units, with logits
+    far beyond the f32 range of exp (up to ~650): every row against the
+    oracle, on block lists drawn by the oracle's selection from a random
+    metric (the attention sees only the lists)."""
+    _cuda()
+    import torch
+    w = MOVING_MAX[name]
+    H.log(f"case moving maximum {name} slope={slope} gain={gain}")
+    x = _moving_max_inputs(w, slope, gain, seed=w.seed + 7)
+    plan = stem.plan_for(w).to("cuda")
+    i = plan.info
+    cub = O.block_layout(w.cu_seqlens, w.block)
+    bud = O.budgets_for(cub, w.sink_blocks, w.k_min, w.rho0, w.tau)
+    rng = np.random.default_rng(w.seed)
+    m = rng.random((w.num_q_heads, int(i.score_elems_per_head)))
+    idx, cnt = O.select(m, cub, bud, w.sink_blocks, kmax=int(i.kmax))
+    q, k, v = H.upload(x)
+    out = torch.empty((i.total_tokens, w.num_q_heads, w.head_dim), dtype=torch.float32, device="cuda")
+    lse = torch.empty((w.num_q_heads, i.total_tokens), dtype=torch.float32, device="cuda")
+    stem.stem_sparse_attn(plan, q, k, v, torch.from_numpy(idx).to("cuda"),
+                          torch.from_numpy(cnt).to("cuda"), out, lse)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = O.sparse_attn(x.q, x.k, x.v, idx, cnt, w.cu_seqlens, w.block)
+    err = H.check_out(out.cpu().numpy(), o_ref, w.dtype, "f32", f"moving maximum {name}")
+    got_lse = lse.cpu().numpy()
+    H.log(f"  output max err {err:.3g}, LSE max err {np.abs(got_lse - lse_ref).max():.3g} "
+          f"(LSE up to {np.abs(lse_ref).max():.0f})")
+    assert np.isfinite(got_lse).all()
+    # The row sum is taken over the bf16-rounded weights (the ones that
+    # multiply V), each within 2^-8 of its f32 value; when one key carries a
+    # row and its weight against the lazily moved reference is not a power of
+    # two, the sum, and so the LSE, keeps up to ln(1 + 2^-8) of that rounding
+    # (on ordinary rows many weights share it and the error is ~1e-6).  f32
+    # logits of magnitude up to ~2e3 add well under 1e-4.
+    lse_bar = float(np.log1p(2.0 ** -8)) + 1e-4
+    assert np.abs(got_lse - lse_ref).max() <= lse_bar
+
+
 # ----------------------------------------------------------------- full size
 
 
